@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+Shared by ``tests/``, ``bench.py`` and ``__graft_entry__.smoke()``.  This module holds
+none of the method's arithmetic: it only draws random numbers, applies the input
+recipe (shifts, constant rows, outlier keys) and casts to the storage dtype, so both
+the GPU path and the CPU oracle receive the very same bits.
+
+Recipe (all draws from NumPy's PCG64, in float32, in the order listed):
+
+* attention: Q, K, V iid N(0, 1) of shape [B, H, N, d]; optionally a fraction of the
+  key rows of every head (chosen without replacement) multiplied by 8, which is
+  exact in both fp32 and bf16; then cast to bf16 by round-to-nearest-even where the
+  workload is bf16.
+* row softmax: x iid N(0, sigma) of shape [rows, cols]; three disjoint row sets of
+  floor(1% of rows) each get +1000 added, -1000 added, or every entry replaced by
+  the row's first entry (an all-equal row).
+* scalar rows: the pages' worked row (scores 0, 1, 2 with values 10, 20, 30), the
+  same with every score +1000, and 390 random rows, ten of each length 1..39, with
+  scores N(0, 2) and values U(-10, 10).
+* sampled query rows for the long-sequence check: per head 1024 distinct rows drawn
+  uniformly from 1..N-2, plus rows 0 and N-1.
+
+The second parameter of N(0, 2) / N(0, 3) is read as the standard deviation.
+"""
+
+import math
+
+import numpy as np
+
+SEED_BASE = 20261202
+
+# The workloads, keyed by what they are.  ``seed`` is SEED_BASE + the workload's
+# position in the list; variants of one workload add a fixed offset.
+CONFIGS = {
+    "attn_f32_b1h1n256d64": dict(kind="attn", dtype="f32", B=1, H=1, N=256, d=64,
+                                 causal=False, seed=SEED_BASE + 0),
+    "softmax_f32_65536x4096": dict(kind="softmax", rows=65536, cols=4096, sigma=3.0,
+                                   seed=SEED_BASE + 1),
+    "softmax_f32_65536x4095": dict(kind="softmax", rows=65536, cols=4095, sigma=3.0,
+                                   seed=SEED_BASE + 1 + 1000),
+    "softmax_f32_65536x1": dict(kind="softmax", rows=65536, cols=1, sigma=3.0,
+                                seed=SEED_BASE + 1 + 2000),
+    "attn_bf16_b4h16n2048d64": dict(kind="attn", dtype="bf16", B=4, H=16, N=2048, d=64,
+                                    causal=False, seed=SEED_BASE + 2),
+    "attn_bf16_causal_b2h32n8192d128": dict(kind="attn", dtype="bf16", B=2, H=32, N=8192,
+                                            d=128, causal=True, seed=SEED_BASE + 3),
+    "attn_bf16_causal_b2h32n8191d128": dict(kind="attn", dtype="bf16", B=2, H=32, N=8191,
+                                            d=128, causal=True, seed=SEED_BASE + 3 + 1000),
+    "attn_bf16_causal_b1h8n131072d128": dict(kind="attn", dtype="bf16", B=1, H=8, N=131072,
+                                             d=128, causal=True, seed=SEED_BASE + 4,
+                                             k_outlier_frac=0.001, k_outlier_scale=8.0,
+                                             sample_rows=1024),
+}
+
+
+def generator(seed):
+    """The one random source: NumPy PCG64 seeded with ``seed``."""
+    return np.random.Generator(np.random.PCG64(int(seed)))
+
+
+def default_scale(d):
+    """1/sqrt(d) rounded to float32, the value every caller passes as ``scale``."""
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _to_torch(a, dtype):
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)  # round-to-nearest-even
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return t
+
+
+def attention_inputs(B, H, N, d, seed, dtype="bf16", k_outlier_frac=0.0,
+                     k_outlier_scale=8.0):
+    """Q, K, V as CPU torch tensors [B, H, N, d] of ``dtype`` ('bf16' or 'f32')."""
+    g = generator(seed)
+    shape = (B, H, N, d)
+    q = g.standard_normal(shape, dtype=np.float32)
+    k = g.standard_normal(shape, dtype=np.float32)
+    v = g.standard_normal(shape, dtype=np.float32)
+    n_out = int(math.floor(k_outlier_frac * N))
+    if n_out:
+        for b in range(B):
+            for h in range(H):
+                idx = g.choice(N, size=n_out, replace=False)
+                k[b, h, idx, :] *= np.float32(k_outlier_scale)
+    return _to_torch(q, dtype), _to_torch(k, dtype), _to_torch(v, dtype)
+
+
+def attention_inputs_for(name):
+    c = CONFIGS[name]
+    return attention_inputs(c["B"], c["H"], c["N"], c["d"], c["seed"], c["dtype"],
+                            c.get("k_outlier_frac", 0.0), c.get("k_outlier_scale", 8.0))
+
+
+def softmax_inputs(rows, cols, seed, sigma=3.0, special_frac=0.01):
+    """x as a CPU float32 torch tensor [rows, cols], plus the special row sets.
+
+    Returns (x, specials) where specials maps 'plus1000', 'minus1000' and
+    'all_equal' to sorted int64 arrays of row indices (disjoint).
+    """
+    import torch
+
+    g = generator(seed)
+    x = g.standard_normal((rows, cols), dtype=np.float32)
+    x *= np.float32(sigma)
+    n_sp = int(math.floor(special_frac * rows))
+    pick = g.choice(rows, size=3 * n_sp, replace=False)
+    specials = {
+        "plus1000": np.sort(pick[:n_sp]),
+        "minus1000": np.sort(pick[n_sp:2 * n_sp]),
+        "all_equal": np.sort(pick[2 * n_sp:]),
+    }
+    x[specials["plus1000"]] += np.float32(1000.0)
+    x[specials["minus1000"]] -= np.float32(1000.0)
+    ae = specials["all_equal"]
+    x[ae] = x[ae, :1]
+    return torch.from_numpy(x), specials
+
+
+def softmax_inputs_for(name):
+    c = CONFIGS[name]
+    return softmax_inputs(c["rows"], c["cols"], c["seed"], c["sigma"])
+
+
+def scalar_rows(seed=SEED_BASE + 0, per_length=10, max_length=39):
+    """The scalar rows: list of (label, scores, values) with Python float lists."""
+    rows = [
+        ("worked", [0.0, 1.0, 2.0], [10.0, 20.0, 30.0]),
+        ("worked_plus1000", [1000.0, 1001.0, 1002.0], [10.0, 20.0, 30.0]),
+    ]
+    g = generator(seed + 500)
+    for n in range(1, max_length + 1):
+        for r in range(per_length):
+            s = g.normal(0.0, 2.0, size=n)
+            v = g.uniform(-10.0, 10.0, size=n)
+            rows.append((f"len{n}_{r}", s.tolist(), v.tolist()))
+    return rows
+
+
+def sampled_query_rows(B, H, N, per_head, seed):
+    """int64 [B, H, per_head + 2]: distinct rows from 1..N-2 per head, plus 0 and N-1."""
+    g = generator(seed + 7)
+    out = np.empty((B, H, per_head + 2), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            mid = g.choice(np.arange(1, N - 1), size=per_head, replace=False)
+            out[b, h] = np.sort(np.concatenate([[0, N - 1], mid]))
+    return out
