@@ -1,0 +1,115 @@
+/*
+ * mi355attn.h — C ABI of libmi355attn.so: exact tiled attention forward and
+ * row-wise online softmax for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (pages cited by title and section):
+ *
+ *   Attention forward, "Softmax numerical stability and IO-aware attention:
+ *   from online normalisation to FlashAttention" (zhouzhq2021.github.io), section 7:
+ *   O = softmax(scale * Q K^T) V, computed one query tile at a time while the
+ *   key/value tiles stream through on-chip memory, keeping a running row maximum m
+ *   and row sum l and rescaling the output accumulator by alpha = exp(m - m_new);
+ *   the N x N score matrix never reaches device memory.  The lihaoran.work
+ *   FlashAttention note, section "the problem starts with the intermediate matrix",
+ *   states the same operation with scale = 1/sqrt(d).
+ *
+ *   Row softmax, same page, sections 3, 4, 4.1 and 4.2: y = exp(x - m) / l per row,
+ *   where the (m, l) state of a row is reduced as a tree with the merge rule
+ *   m = max(m_a, m_b), l = l_a exp(m_a - m) + l_b exp(m_b - m).
+ *
+ * Conventions shared by every entry point:
+ *
+ *   Memory     All pointers are device pointers to memory owned by the caller.  The
+ *              library allocates, frees and copies nothing, keeps no global mutable
+ *              state, and may be called from several host threads at once.
+ *   Streams    `stream` is a hipStream_t passed as void*; NULL means the default
+ *              stream.  Work is enqueued asynchronously on that stream; outputs are
+ *              valid once the caller has synchronised with it.  Nothing here
+ *              synchronises.
+ *   Errors     Arguments are checked before any HIP call.  A bad argument returns
+ *              MI355ATTN_ERR_INVALID_ARG, an unsupported shape or head dimension
+ *              returns MI355ATTN_ERR_UNSUPPORTED, and a failed launch returns
+ *              MI355ATTN_ERR_HIP (mi355attn_last_hip_error() then gives the
+ *              hipError_t of that failure on the calling thread).  On any error no
+ *              output has been written.  mi355attn_strerror() names a code.
+ *   Layout     Dense, row-major, no strides.  Attention tensors are [B, H, N, d]:
+ *              element (b, h, n, t) lives at index ((b * H + h) * N + n) * d + t.
+ *              LSE is [B, H, N] float32.  Row-softmax tensors are [rows, cols].
+ *   Alignment  Attention pointers must be 16-byte aligned; row-softmax pointers 4-byte
+ *              aligned (16-byte aligned rows of a multiple of 4 columns take a faster path).
+ */
+#ifndef MI355ATTN_H
+#define MI355ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MI355ATTN_OK = 0,
+    MI355ATTN_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, bad scale, misaligned or overlapping buffers */
+    MI355ATTN_ERR_UNSUPPORTED = -2, /* head dimension or size this build has no kernel for */
+    MI355ATTN_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * fa_fwd — bf16 attention forward (the hot path).
+ *
+ *   q, k, v  [B, H, N, d] bf16 (raw IEEE bfloat16 bits, 2 bytes each), read only.
+ *   o        [B, H, N, d] bf16, written: O = P V / l rounded once to bf16 (nearest even).
+ *   lse      [B, H, N] float32, written: ln(sum over visible keys j of exp(scale * q_i . k_j)),
+ *            natural log of the scaled scores, = m_i + ln l_i.
+ *   B, H, N  >= 1.  N up to 2^31 - 1 (offsets are computed in 64 bits).
+ *   d        64 or 128; anything else returns MI355ATTN_ERR_UNSUPPORTED.
+ *   scale    finite float multiplying every score before the softmax (callers pass 1/sqrt(d)).
+ *   causal   0: every query sees all N keys.  1: self-attention, query i sees keys j <= i
+ *            (top-left aligned, so no row is empty); tiles wholly above the diagonal are skipped.
+ *   stream   hipStream_t or NULL.
+ *
+ * Arithmetic: Q K^T and P V run on bf16 matrix cores with float32 accumulation; the running
+ * maximum, running sum, rescale factors and the output accumulator stay in float32; P is
+ * rounded to bf16 (nearest even) as the operand of P V.
+ * o must not overlap q, k, v or lse; lse must not overlap any other buffer.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_f32 — float32 attention forward with the same semantics as fa_fwd.
+ *
+ *   q, k, v, o  [B, H, N, d] float32;  lse [B, H, N] float32.
+ *   d           64 or 128.
+ * Every product and sum is an ordinary float32 operation (no reduced-precision operand).
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * online_softmax_rows — y[r, :] = softmax(x[r, :]) for every row r, in float32.
+ *
+ *   x     [rows, cols] float32, read only.
+ *   y     [rows, cols] float32, written.  y == x (in place) is allowed; any other overlap is not.
+ *   rows  >= 0; rows == 0 does nothing and returns MI355ATTN_OK.
+ *   cols  >= 1 and cols <= 1048576 (larger rows return MI355ATTN_ERR_UNSUPPORTED).
+ *
+ * Each row is read once from device memory when it fits on chip (cols <= 16384) and twice
+ * otherwise; it is written once.  Inputs must be finite.
+ */
+int online_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream);
+
+/* Human-readable name of a return code (static string, never NULL). */
+const char* mi355attn_strerror(int code);
+
+/* hipError_t of the last MI355ATTN_ERR_HIP returned on the calling thread (0 if none). */
+int mi355attn_last_hip_error(void);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int mi355attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355ATTN_H */

@@ -1,0 +1,111 @@
+// api.cpp — the extern "C" boundary of libmi355attn.so (declared in include/mi355attn.h).
+//
+// Every argument is validated here, before any HIP call, so bad input comes back as a
+// return code without touching the device.  The launchers enqueue on the caller's
+// stream and never synchronise.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/mi355attn.h"
+#include "launchers.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxSoftmaxCols = 1 << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a + na) and [b, b + nb) intersect.
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+int finish(hipError_t e) {
+    if (e == hipSuccess) return MI355ATTN_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return MI355ATTN_ERR_HIP;
+}
+
+// Checks shared by both attention entry points.  elem = bytes per element of q/k/v/o.
+int check_attention(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                    int H, int N, int d, float scale, uint64_t elem) {
+    if (!q || !k || !v || !o || !lse) return MI355ATTN_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 1 || d < 1) return MI355ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return MI355ATTN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return MI355ATTN_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return MI355ATTN_ERR_UNSUPPORTED;
+    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+    if ((uint64_t)B * (uint64_t)H > (uint64_t)INT_MAX) return MI355ATTN_ERR_UNSUPPORTED;
+    const uint64_t tbytes = rows * (uint64_t)d * elem;
+    const uint64_t lbytes = rows * sizeof(float);
+    if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) || overlaps(o, tbytes, v, tbytes) ||
+        overlaps(o, tbytes, lse, lbytes) || overlaps(lse, lbytes, q, tbytes) ||
+        overlaps(lse, lbytes, k, tbytes) || overlaps(lse, lbytes, v, tbytes))
+        return MI355ATTN_ERR_INVALID_ARG;
+    return MI355ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, void* stream) {
+    const int rc = check_attention(q, k, v, o, lse, B, H, N, d, scale, 2);
+    if (rc != MI355ATTN_OK) return rc;
+    if (causal != 0 && causal != 1) return MI355ATTN_ERR_INVALID_ARG;
+    return finish(mi355::launch_attn_fwd_bf16(q, k, v, o, lse, B, H, N, d, scale, causal != 0,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
+               int d, float scale, int causal, void* stream) {
+    const int rc = check_attention(q, k, v, o, lse, B, H, N, d, scale, 4);
+    if (rc != MI355ATTN_OK) return rc;
+    if (causal != 0 && causal != 1) return MI355ATTN_ERR_INVALID_ARG;
+    return finish(mi355::launch_attn_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal != 0,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int online_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream) {
+    if (rows < 0 || cols < 1) return MI355ATTN_ERR_INVALID_ARG;
+    if (rows == 0) return MI355ATTN_OK;
+    if (!x || !y) return MI355ATTN_ERR_INVALID_ARG;
+    if (cols > kMaxSoftmaxCols) return MI355ATTN_ERR_UNSUPPORTED;
+    if (rows > (int64_t)INT_MAX) return MI355ATTN_ERR_UNSUPPORTED;
+    // 4-byte alignment is enough; the 16-byte vector path is chosen only when both
+    // pointers and the row length allow it.
+    if ((reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(y) & 3u))
+        return MI355ATTN_ERR_INVALID_ARG;
+    const uint64_t bytes = (uint64_t)rows * (uint64_t)cols * sizeof(float);
+    if (x != y && overlaps(x, bytes, y, bytes)) return MI355ATTN_ERR_INVALID_ARG;
+    return finish(mi355::launch_softmax_rows(x, y, rows, cols, static_cast<hipStream_t>(stream)));
+}
+
+const char* mi355attn_strerror(int code) {
+    switch (code) {
+        case MI355ATTN_OK:
+            return "success";
+        case MI355ATTN_ERR_INVALID_ARG:
+            return "invalid argument (null pointer, bad size or scale, misaligned or overlapping buffers)";
+        case MI355ATTN_ERR_UNSUPPORTED:
+            return "unsupported shape (head dimension must be 64 or 128; size limits exceeded)";
+        case MI355ATTN_ERR_HIP:
+            return "HIP runtime error at launch (see mi355attn_last_hip_error)";
+        default:
+            return "unknown mi355attn return code";
+    }
+}
+
+int mi355attn_last_hip_error(void) { return g_last_hip_error; }
+
+int mi355attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,335 @@
+// attn_fwd_bf16.hip — bf16 tiled attention forward on gfx950 matrix cores.
+//
+// Algorithm: "Softmax numerical stability and IO-aware attention" (zhouzhq2021.github.io),
+// section 7: per query tile, initialise m = -inf, l = 0, O = 0; for every key/value
+// tile form S = Q K^T, m_new = max(m, rowmax S), P = exp(S - m_new),
+// alpha = exp(m - m_new), l = alpha l + rowsum P, O = alpha O + P V; finally O / l.
+// Section 8 (FlashAttention-2) adds the choices kept here: the query tile is the outer
+// loop so O is written once, the division by l is deferred to the end, and key tiles
+// wholly above the causal diagonal are skipped.  LSE = m + ln l is written per row.
+//
+// gfx950 mapping (a design of its own, not the pages' warp/shared-memory scheme):
+//
+//   * Block = 4 wavefronts = 128 query rows; each wavefront owns 32 query rows for
+//     the whole key loop.  Key tiles are 64 keys, double-buffered in LDS.
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//     A = a 32-key slice of K (from LDS), B = Q^T (held in registers for the whole
+//     loop).  In the 32x32 accumulator, lane l holds one column, i.e. one query row
+//     (l mod 32), and 16 of its keys; the other 16 keys of that row sit in lane l^32.
+//     So the row max is 31 in-lane maxima plus one exchange, and the row sum needs no
+//     exchange at all until the end (each half keeps a partial l under the same m).
+//   * The output is accumulated transposed too, O^T += V^T P^T: the B operand
+//     (P^T, 8 keys x 1 query per lane) is exactly what the lane already holds after
+//     the exponentials, converted to bf16 with no data movement.  The A operand
+//     (V^T) is read from LDS, where V is stored transposed at staging time with the
+//     keys of every 16-key group ordered 0-3, 8-11, 4-7, 12-15, the order in which
+//     the accumulator hands P to the lanes.  The O^T accumulator keeps one query row
+//     per lane as well, so alpha rescales it with no exchange.
+//   * The rescale of O is skipped when alpha is exactly 1 on every lane of the
+//     wavefront (the running maxima did not move), which is exact.
+//   * Exponentials use the hardware exp2 on scores pre-multiplied by scale * log2 e.
+//   * Block ids are remapped so each of the 8 XCDs (which receive block ids round
+//     robin) walks a contiguous range of (head, query tile) pairs: the key/value
+//     stream of a head is then shared through that XCD's L2.  In causal mode the
+//     tiles of a head run longest-first.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace mi355 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+constexpr int kWaves = 4;
+constexpr int kBM = 32 * kWaves;  // query rows per block
+constexpr int kBN = 64;           // keys per tile
+
+template <int D>
+struct Smem {
+    static constexpr int kStride = D + 8;     // bf16 per K row (16-byte pad against bank conflicts)
+    static constexpr int vStride = kBN + 8;   // bf16 per V^T row
+    uint16_t k[2][kBN * kStride];
+    uint16_t vt[2][D * vStride];
+};
+
+// Position of key r (0..63 within a tile) in a V^T row: inside each 16-key group
+// the 4-key runs are stored in the order 0, 2, 1, 3.
+__device__ __forceinline__ int vt_pos(int r) {
+    const int run = (r >> 2) & 3;
+    const int run_pos = ((run & 1) << 1) | (run >> 1);
+    return (r & ~15) | (run_pos << 2) | (r & 3);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+struct Params {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    int N;
+    int n_qtiles;
+    int n_blocks;
+    float scale_log2;  // scale * log2(e)
+};
+
+// Global -> register staging of one key/value tile (64 keys).
+template <int D>
+struct Stage {
+    static constexpr int kChunks = kBN * D / 8 / 256;        // 16-byte K chunks per thread
+    static constexpr int vUnits = (kBN / 4) * (D / 8);       // (4 keys x 8 dims) V units per tile
+    uint4 kr[kChunks];
+    uint4 vr[4];
+
+    __device__ __forceinline__ void load(const uint16_t* kh, const uint16_t* vh, int j0, int N, int tid) {
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int idx = tid + 256 * c;
+            const int key = j0 + idx / (D / 8);
+            const int col = (idx % (D / 8)) * 8;
+            kr[c] = key < N ? *reinterpret_cast<const uint4*>(kh + (int64_t)key * D + col)
+                            : make_uint4(0, 0, 0, 0);
+        }
+        if (tid < vUnits) {
+            const int kg = tid / (D / 8);
+            const int col = (tid % (D / 8)) * 8;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = j0 + 4 * kg + r;
+                vr[r] = key < N ? *reinterpret_cast<const uint4*>(vh + (int64_t)key * D + col)
+                                : make_uint4(0, 0, 0, 0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(Smem<D>& sm, int buf, int tid) const {
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int idx = tid + 256 * c;
+            const int key = idx / (D / 8);
+            const int col = (idx % (D / 8)) * 8;
+            *reinterpret_cast<uint4*>(&sm.k[buf][key * Smem<D>::kStride + col]) = kr[c];
+        }
+        if (tid < vUnits) {
+            const int kg = tid / (D / 8);
+            const int col = (tid % (D / 8)) * 8;
+            const int pos = vt_pos(4 * kg);
+            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
+            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
+            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
+            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int sh = (e & 1) * 16;
+                const uint32_t a0 = (w0[e >> 1] >> sh) & 0xffffu, a1 = (w1[e >> 1] >> sh) & 0xffffu;
+                const uint32_t a2 = (w2[e >> 1] >> sh) & 0xffffu, a3 = (w3[e >> 1] >> sh) & 0xffffu;
+                uint2 out;
+                out.x = a0 | (a1 << 16);
+                out.y = a2 | (a3 << 16);
+                *reinterpret_cast<uint2*>(&sm.vt[buf][(col + e) * Smem<D>::vStride + pos]) = out;
+            }
+        }
+    }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
+    constexpr int KS = D / 16;  // k-steps of Q K^T
+    constexpr int DB = D / 32;  // 32-wide blocks of the output dimension
+    __shared__ Smem<D> sm;
+
+    // XCD-aware remap: block id b runs on XCD b % 8; give each XCD a contiguous
+    // range of logical ids.
+    const int nb = p.n_blocks;
+    int lid = blockIdx.x;
+    if ((nb & 7) == 0) lid = (lid & 7) * (nb >> 3) + (lid >> 3);
+    const int bh = lid / p.n_qtiles;
+    int qt = lid % p.n_qtiles;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest tiles first
+
+    const int N = p.N;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int half = lane >> 5;
+    const int64_t head = (int64_t)bh * N * D;
+    const uint16_t* kh = p.k + head;
+    const uint16_t* vh = p.v + head;
+
+    const int q0 = qt * kBM;
+    const int qw0 = q0 + 32 * wave;          // this wavefront's first query row
+    const int my_q = qw0 + l32;              // the query row this lane owns
+    const int qw_last = min(qw0 + 31, N - 1);
+    const bool wave_live = qw0 < N;
+
+    // Q^T fragments (B operand): lane supplies Q[my_q][16 s + 8 half + 0..7].
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        if (my_q < N)
+            qf[s] = *reinterpret_cast<const bf16x8*>(p.q + head + (int64_t)my_q * D + 16 * s + 8 * half);
+        else
+            qf[s] = bf16x8{};
+    }
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+    float m = kNegInf;  // running max of scale * log2e * score, this lane's row
+    float l = 0.0f;     // running partial sum over this lane's half of each tile
+
+    const int q_last = min(q0 + kBM - 1, N - 1);
+    const int n_kv = CAUSAL ? (q_last / kBN + 1) : (N + kBN - 1) / kBN;
+
+    Stage<D> stage;
+    stage.load(kh, vh, 0, N, tid);
+    stage.store(sm, 0, tid);
+    __syncthreads();
+
+    for (int j = 0; j < n_kv; ++j) {
+        const int buf = j & 1;
+        const int j0 = j * kBN;
+        if (j + 1 < n_kv) stage.load(kh, vh, j0 + kBN, N, tid);
+
+        const bool active = wave_live && (!CAUSAL || j0 <= qw_last);
+        if (active) {
+            // ---- S^T = K Q^T for the two 32-key halves of the tile
+            f32x16 s[2] = {f32x16{}, f32x16{}};
+            const uint16_t* kb = &sm.k[buf][0];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        kb + (32 * sb + l32) * Smem<D>::kStride + 16 * ks + 8 * half);
+                    s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
+                }
+            }
+
+            // ---- scale into the log2 domain, mask, row max
+            const bool need_mask = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
+            float mt = kNegInf;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float t = s[sb][r] * p.scale_log2;
+                    if (need_mask) {
+                        const int key = j0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
+                        if (key >= N || (CAUSAL && key > my_q)) t = kNegInf;
+                    }
+                    s[sb][r] = t;
+                    mt = fmaxf(mt, t);
+                }
+            }
+            mt = fmaxf(mt, swap_halves(mt));
+            const float m_new = fmaxf(m, mt);
+            const float base = safe_base(m_new);
+            const float alpha = fast_exp2(m - base);  // m = -inf gives 0
+
+            // ---- P = exp2(t - m_new), partial row sums
+            float ps = 0.0f;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = fast_exp2(s[sb][r] - base);
+                    s[sb][r] = e;
+                    ps += e;
+                }
+            }
+            l = alpha * l + ps;
+            m = m_new;
+
+            // ---- rescale O (skipped when no running max moved: alpha == 1 exactly)
+            if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int b = 0; b < DB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+            }
+
+            // ---- P^T fragments: lane's values 8 hb .. 8 hb + 7 of each half-tile
+            bf16x8 pf[4];
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        w[t] = pack_bf16x2(s[sb][8 * hb + 2 * t], s[sb][8 * hb + 2 * t + 1]);
+                    pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(w));
+                }
+            }
+
+            // ---- O^T += V^T P^T
+            const uint16_t* vb = &sm.vt[buf][0];
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                        vb + (32 * b + l32) * Smem<D>::vStride + 16 * g + 8 * half);
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], acc[b], 0, 0, 0);
+                }
+            }
+        }
+
+        if (j + 1 < n_kv) stage.store(sm, buf ^ 1, tid);
+        __syncthreads();
+    }
+
+    if (!wave_live) return;
+    const float l_row = l + swap_halves(l);
+    if (my_q < N) {
+        const float inv = 1.0f / l_row;
+        uint16_t* orow = p.o + head + (int64_t)my_q * D;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint2 w;
+                w.x = pack_bf16x2(acc[b][4 * i + 0] * inv, acc[b][4 * i + 1] * inv);
+                w.y = pack_bf16x2(acc[b][4 * i + 2] * inv, acc[b][4 * i + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + 32 * b + 8 * i + 4 * half) = w;
+            }
+        }
+        if (half == 0) p.lse[(int64_t)bh * N + my_q] = (m + fast_log2(l_row)) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const Params& p, hipStream_t st) {
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                int H, int N, int d, float scale, bool causal, hipStream_t st) {
+    Params p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.o = static_cast<uint16_t*>(o);
+    p.lse = lse;
+    p.N = N;
+    p.n_qtiles = (N + kBM - 1) / kBM;
+    const int64_t blocks = (int64_t)B * H * p.n_qtiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    p.n_blocks = (int)blocks;
+    p.scale_log2 = scale * kLog2e;
+    if (d == 64) return causal ? launch<64, true>(p, st) : launch<64, false>(p, st);
+    if (d == 128) return causal ? launch<128, true>(p, st) : launch<128, false>(p, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mi355

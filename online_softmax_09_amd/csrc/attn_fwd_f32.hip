@@ -1,0 +1,144 @@
+// attn_fwd_f32.hip — float32 tiled attention forward (plain fp32 FMA, no matrix cores).
+//
+// Same algorithm as the bf16 kernel: "Softmax numerical stability and IO-aware
+// attention" (zhouzhq2021.github.io), section 7 — for each query tile, stream the
+// key/value tiles through on-chip memory, keep the running row maximum m and sum l,
+// rescale the output accumulator by alpha = exp(m - m_new) whenever m grows
+// (section 7 stresses that both l and the accumulator take alpha), and divide by l
+// once at the end.  The lihaoran.work FlashAttention note ("why per-block softmaxes
+// cannot be averaged") gives the same (m, l, u) recurrence for one scalar value.
+//
+// Mapping: one 64-lane wavefront per block, one query row per lane.  The key and
+// value tiles are staged in LDS, where every lane reads the same key row (an LDS
+// broadcast).  Scores are kept in their natural units and exponentiated as
+// exp2((s - m) * log2 e): the difference is formed first, so large shifted scores
+// (e.g. every score + 1000) lose no accuracy to the log2 e factor.
+#include "device_common.hpp"
+#include "launchers.hpp"
+
+namespace mi355 {
+namespace {
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(const float* __restrict__ q,
+                                                          const float* __restrict__ k,
+                                                          const float* __restrict__ v,
+                                                          float* __restrict__ o,
+                                                          float* __restrict__ lse, int N,
+                                                          int n_qtiles, float scale) {
+    constexpr int BN = (D <= 64) ? 32 : 16;  // keys per tile
+    __shared__ float4 ks[BN][D / 4];
+    __shared__ float4 vs[BN][D / 4];
+
+    const int64_t bh = blockIdx.x / n_qtiles;
+    const int q0 = (blockIdx.x % n_qtiles) * 64;
+    const int i = q0 + threadIdx.x;  // this lane's query row
+    const bool row_ok = i < N;
+    const int64_t head = bh * (int64_t)N * D;
+
+    float4 qr[D / 4];
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c)
+        qr[c] = row_ok ? reinterpret_cast<const float4*>(q + head + (int64_t)i * D)[c]
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    float4 acc[D / 4];
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float m = kNegInf, l = 0.0f;
+
+    // Causal: keys beyond the block's last query are never visible.
+    const int kv_end = CAUSAL ? min(N, q0 + 64) : N;
+    for (int j0 = 0; j0 < kv_end; j0 += BN) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < BN * (D / 4); idx += 64) {
+            const int r = idx / (D / 4), c = idx % (D / 4);
+            const int key = j0 + r;
+            const bool ok = key < N;
+            const int64_t off = head + (int64_t)key * D;
+            ks[r][c] = ok ? reinterpret_cast<const float4*>(k + off)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            vs[r][c] = ok ? reinterpret_cast<const float4*>(v + off)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        __syncthreads();
+
+        float s[BN];
+        float mt = kNegInf;
+#pragma unroll
+        for (int jj = 0; jj < BN; ++jj) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int c = 0; c < D / 4; ++c) {
+                const float4 kk = ks[jj][c];
+                dot = fmaf(qr[c].x, kk.x, dot);
+                dot = fmaf(qr[c].y, kk.y, dot);
+                dot = fmaf(qr[c].z, kk.z, dot);
+                dot = fmaf(qr[c].w, kk.w, dot);
+            }
+            const int key = j0 + jj;
+            const bool visible = key < N && (!CAUSAL || key <= i);
+            s[jj] = visible ? dot * scale : kNegInf;
+            mt = fmaxf(mt, s[jj]);
+        }
+        const float m_new = fmaxf(m, mt);
+        const float base = safe_base(m_new);
+        const float alpha = (m == kNegInf) ? 0.0f : fast_exp2((m - base) * kLog2e);
+        float ps = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < BN; ++jj) {
+            s[jj] = fast_exp2((s[jj] - base) * kLog2e);
+            ps += s[jj];
+        }
+        l = alpha * l + ps;
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+            float4 a = acc[c];
+            a.x *= alpha;
+            a.y *= alpha;
+            a.z *= alpha;
+            a.w *= alpha;
+#pragma unroll
+            for (int jj = 0; jj < BN; ++jj) {
+                const float4 vv = vs[jj][c];
+                a.x = fmaf(s[jj], vv.x, a.x);
+                a.y = fmaf(s[jj], vv.y, a.y);
+                a.z = fmaf(s[jj], vv.z, a.z);
+                a.w = fmaf(s[jj], vv.w, a.w);
+            }
+            acc[c] = a;
+        }
+        m = m_new;
+    }
+
+    if (row_ok) {
+        float4* orow = reinterpret_cast<float4*>(o + head + (int64_t)i * D);
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c)
+            orow[c] = make_float4(acc[c].x / l, acc[c].y / l, acc[c].z / l, acc[c].w / l);
+        lse[bh * N + i] = m + fast_log2(l) * kLn2;
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const float* q, const float* k, const float* v, float* o, float* lse, int BH, int N,
+                  float scale, hipStream_t st) {
+    const int n_qtiles = (N + 63) / 64;
+    const int64_t blocks = (int64_t)BH * n_qtiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(64), 0, st, q, k,
+                       v, o, lse, N, n_qtiles, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                               int B, int H, int N, int d, float scale, bool causal, hipStream_t st) {
+    const int BH = B * H;
+    if (d == 64) return causal ? launch<64, true>(q, k, v, o, lse, BH, N, scale, st)
+                               : launch<64, false>(q, k, v, o, lse, BH, N, scale, st);
+    if (d == 128) return causal ? launch<128, true>(q, k, v, o, lse, BH, N, scale, st)
+                                : launch<128, false>(q, k, v, o, lse, BH, N, scale, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mi355

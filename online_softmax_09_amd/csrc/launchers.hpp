@@ -1,0 +1,30 @@
+// launchers.hpp — host-side entry points of the kernels, called by the C ABI layer
+// (api.cpp) after it has validated every argument.  Each returns the hipError_t of
+// its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355 {
+
+// Which row-softmax variant a shape takes.
+struct SoftmaxPlan {
+    enum Kind { kSmall, kReg, kStream } kind;
+    int group;  // kSmall: lanes per row
+    int waves;  // kReg: wavefronts per row (1 or 4)
+    int nv;     // kReg: units per lane
+    bool vec4;  // 16-byte units (cols % 4 == 0 and both pointers 16-byte aligned)
+};
+
+SoftmaxPlan softmax_plan(const float* x, const float* y, int64_t cols);
+
+hipError_t launch_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, hipStream_t st);
+
+hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                               int B, int H, int N, int d, float scale, bool causal, hipStream_t st);
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int N, int d, float scale, bool causal, hipStream_t st);
+
+}  // namespace mi355

@@ -1,0 +1,76 @@
+"""Shared helpers for the GPU parity tests: device handling and error metrics.
+
+The tolerances are the gates stated for this path: float32 paths within 1e-5 absolute;
+bf16 attention within 2e-2 absolute on O and 1e-2 absolute on LSE.
+"""
+
+import os
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+TOL_F32 = 1e-5
+TOL_BF16_O = 2e-2
+TOL_BF16_LSE = 1e-2
+
+
+def need_gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import online_softmax_09_amd._lib as L
+
+    L.load()  # raises if the library is missing: no silent fallback
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def max_abs(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def max_rel(got, ref, floor):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor))) if ref.size else 0.0
+
+
+def oracle_workers():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return 4
+
+
+def oracle_rows_per_head(q, k, v, scale, causal, rows):
+    """oracle.attention_rows evaluated head by head on a thread pool (NumPy releases
+    the GIL in its matrix products and exponentials); rows is [B, H, R]."""
+    import oracle
+
+    B, H = q.shape[:2]
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        return oracle.attention_rows(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                     scale, causal, rows=rows[b:b + 1, h:h + 1])
+
+    with ThreadPoolExecutor(max_workers=oracle_workers()) as ex:
+        res = list(ex.map(one, jobs))
+    R = rows.shape[2]
+    d = q.shape[3]
+    o = np.empty((B, H, R, d))
+    lse = np.empty((B, H, R))
+    for (b, h), (ob, lb) in zip(jobs, res):
+        o[b, h] = ob[0, 0]
+        lse[b, h] = lb[0, 0]
+    return o, lse

@@ -1,0 +1,97 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments with the documented codes before any HIP call.
+
+Every call here fails validation on purpose (fake, never-dereferenced pointers), so
+no kernel is ever launched and no GPU is needed.
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from online_softmax_09_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355attn.h")
+
+INVALID, UNSUPPORTED, OK = _lib.ERR_INVALID_ARG, _lib.ERR_UNSUPPORTED, _lib.OK
+
+# Fake device addresses: 16-byte aligned, far apart, never dereferenced.
+A, Bp, C, D, E = (0x100000000 * (i + 1) for i in range(5))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libmi355attn.so not built")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    assert set(fns) == set(_lib.SIGNATURES), fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_version_and_strerror(lib):
+    assert lib.mi355attn_version() >= 100
+    for code in (OK, INVALID, UNSUPPORTED, _lib.ERR_HIP, 12345):
+        assert isinstance(_lib.strerror(code), str) and _lib.strerror(code)
+    assert lib.mi355attn_last_hip_error() == 0
+
+
+def _fa(lib, entry, q=A, k=Bp, v=C, o=D, lse=E, B=1, H=1, N=16, d=64, scale=0.125, causal=0):
+    return getattr(lib, entry)(q, k, v, o, lse, B, H, N, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+def test_attention_argument_checks(lib, entry):
+    assert _fa(lib, entry, q=None) == INVALID
+    assert _fa(lib, entry, k=None) == INVALID
+    assert _fa(lib, entry, v=None) == INVALID
+    assert _fa(lib, entry, o=None) == INVALID
+    assert _fa(lib, entry, lse=None) == INVALID
+    for bad in (dict(B=0), dict(H=0), dict(N=0), dict(B=-1), dict(d=0)):
+        assert _fa(lib, entry, **bad) == INVALID, bad
+    for s in (math.inf, -math.inf, math.nan):
+        assert _fa(lib, entry, scale=s) == INVALID
+    assert _fa(lib, entry, causal=2) == INVALID
+    assert _fa(lib, entry, q=A + 8) == INVALID          # misaligned
+    assert _fa(lib, entry, lse=E + 4) == INVALID
+    assert _fa(lib, entry, o=A + 64) == INVALID         # o overlaps q
+    assert _fa(lib, entry, lse=Bp + 16) == INVALID      # lse overlaps k
+    for d in (32, 96, 256, 65):
+        assert _fa(lib, entry, d=d) == UNSUPPORTED, d
+    assert _fa(lib, entry, B=1 << 16, H=1 << 16) == UNSUPPORTED
+
+
+def test_softmax_argument_checks(lib):
+    f = lib.online_softmax_rows
+    assert f(A, Bp, 0, 16, None) == OK            # no rows: nothing to do, no HIP call
+    assert f(None, None, 0, 16, None) == OK
+    assert f(A, Bp, -1, 16, None) == INVALID
+    assert f(A, Bp, 4, 0, None) == INVALID
+    assert f(None, Bp, 4, 16, None) == INVALID
+    assert f(A, None, 4, 16, None) == INVALID
+    assert f(A + 2, Bp, 4, 16, None) == INVALID   # not even 4-byte aligned
+    assert f(A, A + 16, 4, 16, None) == INVALID   # partial overlap
+    assert f(A, Bp, 4, (1 << 20) + 1, None) == UNSUPPORTED
+    assert f(A, Bp, 1 << 31, 4, None) == UNSUPPORTED

@@ -1,0 +1,134 @@
+"""GPU parity of online_softmax_rows (through the C ABI) against the float64 oracle.
+
+Gate: max |y_gpu - y_oracle| <= 1e-5 on every element compared.  Bitwise identities
+where the arithmetic is exact: all-equal rows give exactly 1/cols when cols is a power
+of two, one-column rows give exactly 1.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import online_softmax_09_amd as osm
+import oracle
+import workloads
+from parity import TOL_F32, max_abs, max_rel, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_err(x_cpu, y_cpu, chunk=8192):
+    """max abs and max rel (floor 1e-6) error, the oracle evaluated chunk by chunk."""
+    xa, ya = x_cpu.numpy(), y_cpu.numpy()
+    ea, er = 0.0, 0.0
+    for r0 in range(0, xa.shape[0], chunk):
+        ref, _, _ = oracle.softmax_rows(xa[r0:r0 + chunk])
+        ea = max(ea, max_abs(ya[r0:r0 + chunk], ref))
+        er = max(er, max_rel(ya[r0:r0 + chunk], ref, 1e-6))
+    return ea, er
+
+
+def _run(x_cpu, dev):
+    y = osm.online_softmax_rows(x_cpu.to(dev))
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+@pytest.mark.parametrize("name", ["softmax_f32_65536x4096", "softmax_f32_65536x4095"])
+def test_full_size_workloads(name):
+    dev = need_gpu()
+    x, sp = workloads.softmax_inputs_for(name)
+    say(f"case {name}: rows={x.shape[0]} cols={x.shape[1]}")
+    y = _run(x, dev)
+    ea, er = _oracle_err(x, y)
+    say(f"  max abs err {ea:.3e}  max rel err {er:.3e}")
+    assert ea <= TOL_F32
+    cols = x.shape[1]
+    ae = torch.from_numpy(sp["all_equal"])
+    if cols & (cols - 1) == 0:
+        assert torch.all(y[ae] == 1.0 / cols)  # exact: exp(0) = 1 and l = cols
+    assert torch.all(torch.isfinite(y))
+
+
+def test_one_column_rows_are_exactly_one():
+    dev = need_gpu()
+    x, _ = workloads.softmax_inputs_for("softmax_f32_65536x1")
+    say("case softmax_f32_65536x1")
+    y = _run(x, dev)
+    assert torch.all(y == 1.0)
+
+
+# Every kernel variant: short rows (lane groups), one wavefront per row, four
+# wavefronts per row (LDS merge), streaming; 16-byte and 4-byte paths.
+COLS = [1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 1000, 1023, 1024, 1025,
+        2048, 4095, 4096, 4097, 8192, 12000, 16383, 16384, 16385, 40000, 65536]
+
+
+@pytest.mark.parametrize("cols", COLS)
+def test_shapes(cols):
+    dev = need_gpu()
+    rows = 37
+    x, _ = workloads.softmax_inputs(rows, cols, seed=workloads.SEED_BASE + 4000 + cols,
+                                    special_frac=0.1)
+    say(f"case rows={rows} cols={cols}")
+    y = _run(x, dev)
+    ea, _ = _oracle_err(x, y)
+    assert ea <= TOL_F32, ea
+
+
+def test_longest_rows():
+    dev = need_gpu()
+    cols = 1 << 20
+    x, _ = workloads.softmax_inputs(3, cols, seed=workloads.SEED_BASE + 4100)
+    say(f"case rows=3 cols={cols}")
+    y = _run(x, dev)
+    ea, _ = _oracle_err(x, y)
+    assert ea <= TOL_F32, ea
+
+
+def test_in_place():
+    dev = need_gpu()
+    x, _ = workloads.softmax_inputs(500, 4096, seed=workloads.SEED_BASE + 4200)
+    say("case in place 500 x 4096")
+    xd = x.to(dev)
+    out = osm.online_softmax_rows(xd, out=xd)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == xd.data_ptr()
+    ea, _ = _oracle_err(x, xd.cpu())
+    assert ea <= TOL_F32
+
+
+@pytest.mark.parametrize("cols", [4096, 1000, 7])
+def test_unaligned_rows(cols):
+    # Base pointer offset by one float: the 16-byte path must not be taken.
+    dev = need_gpu()
+    rows = 64
+    x, _ = workloads.softmax_inputs(rows, cols, seed=workloads.SEED_BASE + 4300 + cols)
+    say(f"case unaligned rows={rows} cols={cols}")
+    buf = torch.empty(rows * cols + 1, dtype=torch.float32, device=dev)
+    xd = buf[1:].view(rows, cols)
+    xd.copy_(x.to(dev))
+    obuf = torch.empty(rows * cols + 1, dtype=torch.float32, device=dev)
+    yd = obuf[1:].view(rows, cols)
+    osm.online_softmax_rows(xd, out=yd)
+    torch.cuda.synchronize()
+    ea, _ = _oracle_err(x, yd.cpu())
+    assert ea <= TOL_F32
+
+
+def test_empty_batch():
+    dev = need_gpu()
+    x = torch.empty((0, 128), dtype=torch.float32, device=dev)
+    y = osm.online_softmax_rows(x)
+    assert y.shape == (0, 128)
+
+
+def test_repeat_runs_bitwise_identical():
+    dev = need_gpu()
+    x, _ = workloads.softmax_inputs(2048, 4096, seed=workloads.SEED_BASE + 4400)
+    say("case determinism 2048 x 4096")
+    xd = x.to(dev)
+    a = osm.online_softmax_rows(xd)
+    b = osm.online_softmax_rows(xd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
