@@ -20,11 +20,15 @@
 //     exchange at all until the end (each half keeps a partial l under the same m).
 //   * The output is accumulated transposed too, O^T += V^T P^T: the B operand
 //     (P^T, 8 keys x 1 query per lane) is exactly what the lane already holds after
-//     the exponentials, converted to bf16 with no data movement.  The A operand
-//     (V^T) is read from LDS, where V is stored transposed at staging time with the
-//     keys of every 16-key group ordered 0-3, 8-11, 4-7, 12-15, the order in which
-//     the accumulator hands P to the lanes.  The O^T accumulator keeps one query row
-//     per lane as well, so alpha rescales it with no exchange.
+//     the exponentials, converted to bf16 with no data movement.  V is staged in LDS
+//     row-major, exactly like K, and the A operand (V^T) is read with the gfx950
+//     transposing LDS load ds_read_b64_tr_b16: two of them give a lane the 8 keys
+//     (4h..4h+3 and 8+4h..8+4h+3 of a 16-key group) of its output column, the order
+//     in which the S^T accumulator hands P to the lanes.  The O^T accumulator keeps
+//     one query row per lane as well, so alpha rescales it with no exchange.
+//   * LDS row strides: K rows are D*2+16 bytes and V rows D*2+64 bytes, the paddings
+//     under which the 16-byte K reads and the transposing V reads are free of bank
+//     conflicts on gfx950's LDS.
 //   * The rescale of O is skipped when alpha is exactly 1 on every lane of the
 //     wavefront (the running maxima did not move), which is exact.
 //   * Exponentials use the hardware exp2 on scores pre-multiplied by scale * log2 e.
@@ -47,19 +51,11 @@ constexpr int kBN = 64;           // keys per tile
 
 template <int D>
 struct Smem {
-    static constexpr int kStride = D + 8;     // bf16 per K row (16-byte pad against bank conflicts)
-    static constexpr int vStride = kBN + 8;   // bf16 per V^T row
+    static constexpr int kStride = D + 8;    // bf16 per K row
+    static constexpr int vStride = D + 32;   // bf16 per V row
     uint16_t k[2][kBN * kStride];
-    uint16_t vt[2][D * vStride];
+    uint16_t v[2][kBN * vStride];
 };
-
-// Position of key r (0..63 within a tile) in a V^T row: inside each 16-key group
-// the 4-key runs are stored in the order 0, 2, 1, 3.
-__device__ __forceinline__ int vt_pos(int r) {
-    const int run = (r >> 2) & 3;
-    const int run_pos = ((run & 1) << 1) | (run >> 1);
-    return (r & ~15) | (run_pos << 2) | (r & 3);
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
@@ -78,32 +74,25 @@ struct Params {
     float scale_log2;  // scale * log2(e)
 };
 
-// Global -> register staging of one key/value tile (64 keys).
+// Global -> register -> LDS staging of one key/value tile (64 keys x D), both
+// row-major, 16 bytes per access: consecutive threads take consecutive 16-byte
+// chunks of a row, so global reads are fully coalesced and LDS writes are free of
+// bank conflicts.
 template <int D>
 struct Stage {
-    static constexpr int kChunks = kBN * D / 8 / 256;        // 16-byte K chunks per thread
-    static constexpr int vUnits = (kBN / 4) * (D / 8);       // (4 keys x 8 dims) V units per tile
+    static constexpr int kChunks = kBN * D / 8 / 256;  // 16-byte chunks per thread per tensor
     uint4 kr[kChunks];
-    uint4 vr[4];
+    uint4 vr[kChunks];
 
     __device__ __forceinline__ void load(const uint16_t* kh, const uint16_t* vh, int j0, int N, int tid) {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int idx = tid + 256 * c;
             const int key = j0 + idx / (D / 8);
-            const int col = (idx % (D / 8)) * 8;
-            kr[c] = key < N ? *reinterpret_cast<const uint4*>(kh + (int64_t)key * D + col)
-                            : make_uint4(0, 0, 0, 0);
-        }
-        if (tid < vUnits) {
-            const int kg = tid / (D / 8);
-            const int col = (tid % (D / 8)) * 8;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = j0 + 4 * kg + r;
-                vr[r] = key < N ? *reinterpret_cast<const uint4*>(vh + (int64_t)key * D + col)
-                                : make_uint4(0, 0, 0, 0);
-            }
+            const int64_t off = (int64_t)key * D + (idx % (D / 8)) * 8;
+            const bool ok = key < N;
+            kr[c] = ok ? *reinterpret_cast<const uint4*>(kh + off) : make_uint4(0, 0, 0, 0);
+            vr[c] = ok ? *reinterpret_cast<const uint4*>(vh + off) : make_uint4(0, 0, 0, 0);
         }
     }
 
@@ -114,28 +103,20 @@ struct Stage {
             const int key = idx / (D / 8);
             const int col = (idx % (D / 8)) * 8;
             *reinterpret_cast<uint4*>(&sm.k[buf][key * Smem<D>::kStride + col]) = kr[c];
-        }
-        if (tid < vUnits) {
-            const int kg = tid / (D / 8);
-            const int col = (tid % (D / 8)) * 8;
-            const int pos = vt_pos(4 * kg);
-            const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[0]);
-            const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[1]);
-            const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[2]);
-            const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[3]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int sh = (e & 1) * 16;
-                const uint32_t a0 = (w0[e >> 1] >> sh) & 0xffffu, a1 = (w1[e >> 1] >> sh) & 0xffffu;
-                const uint32_t a2 = (w2[e >> 1] >> sh) & 0xffffu, a3 = (w3[e >> 1] >> sh) & 0xffffu;
-                uint2 out;
-                out.x = a0 | (a1 << 16);
-                out.y = a2 | (a3 << 16);
-                *reinterpret_cast<uint2*>(&sm.vt[buf][(col + e) * Smem<D>::vStride + pos]) = out;
-            }
+            *reinterpret_cast<uint4*>(&sm.v[buf][key * Smem<D>::vStride + col]) = vr[c];
         }
     }
 };
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS load: within each group of 16 lanes, lane i receives element i % 4
+// of the 8-byte blocks addressed by lanes i / 4 + 4 k, k = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) uint16_t lds_u16;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_u16*)(p));
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
@@ -158,6 +139,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int half = lane >> 5;
+    // Lane's block for the transposing V reads: row 4 half + (lane % 16) / 4 of the
+    // key group, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of the output block.
+    const int v_lane_off = (4 * half + ((lane & 15) >> 2)) * Smem<D>::vStride +
+                           16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int64_t head = (int64_t)bh * N * D;
     const uint16_t* kh = p.k + head;
     const uint16_t* vh = p.v + head;
@@ -269,14 +254,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
                 }
             }
 
-            // ---- O^T += V^T P^T
-            const uint16_t* vb = &sm.vt[buf][0];
+            // ---- O^T += V^T P^T.  A operand for output rows 32 b .. 32 b + 31 and key
+            // group g: lane l needs V[16 g + 4 half + t][32 b + l32] (t = 0..3) and
+            // V[16 g + 8 + 4 half + t][32 b + l32]; each lane of a 16-lane group
+            // points at one 4-element block of those rows (see v_lane_off).
+            const uint16_t* vb = &sm.v[buf][v_lane_off];
 #pragma unroll
             for (int b = 0; b < DB; ++b) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        vb + (32 * b + l32) * Smem<D>::vStride + 16 * g + 8 * half);
+                    const uint16_t* pa = vb + 16 * g * Smem<D>::vStride + 32 * b;
+                    const i16x4 lo = lds_read_tr16(pa);
+                    const i16x4 hi = lds_read_tr16(pa + 8 * Smem<D>::vStride);
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], acc[b], 0, 0, 0);
                 }
             }
