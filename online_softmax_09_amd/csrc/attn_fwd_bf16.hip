@@ -44,6 +44,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per block
@@ -71,7 +73,8 @@ struct Params {
     int N;
     int n_qtiles;
     int n_blocks;
-    float scale_log2;  // scale * log2(e)
+    float scale_log2;  // |scale| * log2(e)
+    int negate_q;      // scale < 0
 };
 
 // Global -> register -> LDS staging of one key/value tile (64 keys x D), both
@@ -81,18 +84,19 @@ struct Params {
 template <int D>
 struct Stage {
     static constexpr int kChunks = kBN * D / 8 / 256;  // 16-byte chunks per thread per tensor
-    uint4 kr[kChunks];
-    uint4 vr[kChunks];
+    u32x4 kr[kChunks];
+    u32x4 vr[kChunks];
 
     __device__ __forceinline__ void load(const uint16_t* kh, const uint16_t* vh, int j0, int N, int tid) {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int idx = tid + 256 * c;
-            const int key = j0 + idx / (D / 8);
+            // Rows past the end re-read row N-1: their scores are masked to -inf and
+            // their probabilities are 0, so any finite content will do.
+            const int key = min(j0 + idx / (D / 8), N - 1);
             const int64_t off = (int64_t)key * D + (idx % (D / 8)) * 8;
-            const bool ok = key < N;
-            kr[c] = ok ? *reinterpret_cast<const uint4*>(kh + off) : make_uint4(0, 0, 0, 0);
-            vr[c] = ok ? *reinterpret_cast<const uint4*>(vh + off) : make_uint4(0, 0, 0, 0);
+            kr[c] = *reinterpret_cast<const u32x4*>(kh + off);
+            vr[c] = *reinterpret_cast<const u32x4*>(vh + off);
         }
     }
 
@@ -102,8 +106,8 @@ struct Stage {
             const int idx = tid + 256 * c;
             const int key = idx / (D / 8);
             const int col = (idx % (D / 8)) * 8;
-            *reinterpret_cast<uint4*>(&sm.k[buf][key * Smem<D>::kStride + col]) = kr[c];
-            *reinterpret_cast<uint4*>(&sm.v[buf][key * Smem<D>::vStride + col]) = vr[c];
+            *reinterpret_cast<u32x4*>(&sm.k[buf][key * Smem<D>::kStride + col]) = kr[c];
+            *reinterpret_cast<u32x4*>(&sm.v[buf][key * Smem<D>::vStride + col]) = vr[c];
         }
     }
 };
@@ -154,13 +158,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     const bool wave_live = qw0 < N;
 
     // Q^T fragments (B operand): lane supplies Q[my_q][16 s + 8 half + 0..7].
+    // With a negative scale the query is negated (exact in bf16) and |scale| used, so
+    // the row maximum of the raw products is the maximum of the scaled scores.
     bf16x8 qf[KS];
+    const uint32_t qsign = p.negate_q ? 0x80008000u : 0u;
+    const int q_row = min(my_q, N - 1);  // rows past the end compute garbage, never stored
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        if (my_q < N)
-            qf[s] = *reinterpret_cast<const bf16x8*>(p.q + head + (int64_t)my_q * D + 16 * s + 8 * half);
-        else
-            qf[s] = bf16x8{};
+        const u32x4 w = *reinterpret_cast<const u32x4*>(p.q + head + (int64_t)q_row * D + 16 * s + 8 * half);
+        qf[s] = __builtin_bit_cast(bf16x8, w ^ qsign);
     }
 
     f32x16 acc[DB];
@@ -197,34 +203,41 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
                 }
             }
 
-            // ---- scale into the log2 domain, mask, row max
+            // ---- row max of the raw products (scale >= 0 after the sign flip of Q);
+            // on diagonal / ragged tiles hidden keys take no part.
             const bool need_mask = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
+            int key_lim = N - 1;  // last visible key of this lane's row
+            if (CAUSAL) key_lim = min(key_lim, my_q);
+            const int key0 = j0 + 4 * half;  // key of s[0][0]
             float mt = kNegInf;
+            if (need_mask) {
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
+                for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float t = s[sb][r] * p.scale_log2;
-                    if (need_mask) {
-                        const int key = j0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-                        if (key >= N || (CAUSAL && key > my_q)) t = kNegInf;
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = key0 + 32 * sb + 8 * (r >> 2) + (r & 3);
+                        s[sb][r] = key <= key_lim ? s[sb][r] : kNegInf;
                     }
-                    s[sb][r] = t;
-                    mt = fmaxf(mt, t);
-                }
             }
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
             mt = fmaxf(mt, swap_halves(mt));
-            const float m_new = fmaxf(m, mt);
+            // m is kept in log2 units of the scaled score: c * max(raw), c = |scale| log2 e
+            const float m_new = fmaxf(m, mt * p.scale_log2);
             const float base = safe_base(m_new);
             const float alpha = fast_exp2(m - base);  // m = -inf gives 0
 
-            // ---- P = exp2(t - m_new), partial row sums
+            // ---- P = exp2(c s - m_new) with one FMA per score, partial row sums.
+            // Hidden keys get exactly 0 (not exp2 of c * -inf, which is NaN at c = 0).
             float ps = 0.0f;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float e = fast_exp2(s[sb][r] - base);
+                    float e = fast_exp2(fmaf(s[sb][r], p.scale_log2, -base));
+                    if (need_mask) e = s[sb][r] == kNegInf ? 0.0f : e;
                     s[sb][r] = e;
                     ps += e;
                 }
@@ -246,11 +259,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
             for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
-                    uint32_t w[4];
+                    u32x4 w;
 #pragma unroll
                     for (int t = 0; t < 4; ++t)
                         w[t] = pack_bf16x2(s[sb][8 * hb + 2 * t], s[sb][8 * hb + 2 * t + 1]);
-                    pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(w));
+                    pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
                 }
             }
 
@@ -286,10 +299,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
         for (int b = 0; b < DB; ++b) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                uint2 w;
-                w.x = pack_bf16x2(acc[b][4 * i + 0] * inv, acc[b][4 * i + 1] * inv);
-                w.y = pack_bf16x2(acc[b][4 * i + 2] * inv, acc[b][4 * i + 3] * inv);
-                *reinterpret_cast<uint2*>(orow + 32 * b + 8 * i + 4 * half) = w;
+                u32x2 w;
+                w[0] = pack_bf16x2(acc[b][4 * i + 0] * inv, acc[b][4 * i + 1] * inv);
+                w[1] = pack_bf16x2(acc[b][4 * i + 2] * inv, acc[b][4 * i + 3] * inv);
+                *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * i + 4 * half) = w;
             }
         }
         if (half == 0) p.lse[(int64_t)bh * N + my_q] = (m + fast_log2(l_row)) * kLn2;
@@ -317,7 +330,8 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
     const int64_t blocks = (int64_t)B * H * p.n_qtiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     p.n_blocks = (int)blocks;
-    p.scale_log2 = scale * kLog2e;
+    p.scale_log2 = fabsf(scale) * kLog2e;
+    p.negate_q = scale < 0.0f;
     if (d == 64) return causal ? launch<64, true>(p, st) : launch<64, false>(p, st);
     if (d == 128) return causal ? launch<128, true>(p, st) : launch<128, false>(p, st);
     return hipErrorInvalidValue;

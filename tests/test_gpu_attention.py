@@ -244,3 +244,25 @@ def test_unsupported_head_dim_is_an_error():
     q = torch.zeros(1, 1, 16, 96, dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="unsupported"):
         osm.fa_fwd(q, q.clone(), q.clone())
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0883883461356163, 0.5])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("fn,dtype,tol_o,tol_l", [("fa_fwd", "bf16", TOL_BF16_O, TOL_BF16_LSE),
+                                                   ("fa_fwd_f32", "f32", TOL_F32, TOL_F32)])
+def test_scale_edge_cases(fn, dtype, tol_o, tol_l, causal, scale):
+    """scale = 0 (uniform weights over the visible keys), negative and large scales.
+
+    The float32 score error grows with |scale| * sqrt(d) (a d-term dot product of
+    N(0, 1) entries, times scale), so the float32 gate is widened by that factor when
+    it exceeds 1; at scale = 1/sqrt(d) it is the plain 1e-5."""
+    dev = need_gpu()
+    q, k, v = workloads.attention_inputs(1, 2, 333, 128, seed=workloads.SEED_BASE + 7200, dtype=dtype)
+    say(f"case {fn} scale={scale} causal={causal}")
+    o, lse = _gpu(getattr(osm, fn), q, k, v, scale, causal, dev)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale, causal)
+    eo, el = _report(fn, o, lse, o_ref, lse_ref, 1e-3)
+    if dtype == "f32":
+        widen = max(1.0, abs(scale) * math.sqrt(q.shape[-1]))
+        tol_o, tol_l = tol_o * widen, tol_l * widen
+    assert eo <= tol_o and el <= tol_l
