@@ -29,8 +29,10 @@
 //   * LDS row strides: K rows are D*2+16 bytes and V rows D*2+64 bytes, the paddings
 //     under which the 16-byte K reads and the transposing V reads are free of bank
 //     conflicts on gfx950's LDS.
-//   * The rescale of O is skipped when alpha is exactly 1 on every lane of the
-//     wavefront (the running maxima did not move), which is exact.
+//   * The row's reference maximum m moves lazily: only when a tile's maximum exceeds
+//     it by more than 2^8 (kLazy).  Until then alpha is exactly 1 and the rescale of O
+//     is skipped (decided per wavefront); P stays at most 2^8.  The result O / l and
+//     LSE = m + ln l do not depend on which reference m is used.
 //   * Exponentials use the hardware exp2 on scores pre-multiplied by scale * log2 e.
 //   * Block ids are remapped so each of the 8 XCDs (which receive block ids round
 //     robin) walks a contiguous range of (head, query tile) pairs: the key/value
@@ -59,10 +61,18 @@ struct Smem {
     uint16_t v[2][kBN * vStride];
 };
 
+// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+
+// The reference maximum of a row moves only when a tile's maximum exceeds it by more
+// than this many powers of two; until then the probabilities exp2(c s - m) stay at
+// most 2^kLazy (far from overflow) and O and l keep their scale, so the rescale of O
+// is skipped.  O / l and LSE = m + log l are the same for any reference m.
+constexpr float kLazy = 8.0f;
 
 struct Params {
     const uint16_t* q;
@@ -77,37 +87,30 @@ struct Params {
     int negate_q;      // scale < 0
 };
 
-// Global -> register -> LDS staging of one key/value tile (64 keys x D), both
-// row-major, 16 bytes per access: consecutive threads take consecutive 16-byte
-// chunks of a row, so global reads are fully coalesced and LDS writes are free of
-// bank conflicts.
+// Global -> register -> LDS staging of one 64-key tile of K or V (64 x D, row-major),
+// 16 bytes per access: consecutive threads take consecutive 16-byte chunks of a row,
+// so global reads are fully coalesced and LDS writes are free of bank conflicts.
 template <int D>
-struct Stage {
-    static constexpr int kChunks = kBN * D / 8 / 256;  // 16-byte chunks per thread per tensor
-    u32x4 kr[kChunks];
-    u32x4 vr[kChunks];
+struct Prefetch {
+    static constexpr int kChunks = kBN * D / 8 / 256;  // 16-byte chunks per thread
+    u32x4 r[kChunks];
 
-    __device__ __forceinline__ void load(const uint16_t* kh, const uint16_t* vh, int j0, int N, int tid) {
+    __device__ __forceinline__ void load(const uint16_t* base, int j0, int N, int tid) {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int idx = tid + 256 * c;
             // Rows past the end re-read row N-1: their scores are masked to -inf and
             // their probabilities are 0, so any finite content will do.
             const int key = min(j0 + idx / (D / 8), N - 1);
-            const int64_t off = (int64_t)key * D + (idx % (D / 8)) * 8;
-            kr[c] = *reinterpret_cast<const u32x4*>(kh + off);
-            vr[c] = *reinterpret_cast<const u32x4*>(vh + off);
+            r[c] = *reinterpret_cast<const u32x4*>(base + (int64_t)key * D + (idx % (D / 8)) * 8);
         }
     }
 
-    __device__ __forceinline__ void store(Smem<D>& sm, int buf, int tid) const {
+    __device__ __forceinline__ void store(uint16_t* tile, int stride, int tid) const {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int idx = tid + 256 * c;
-            const int key = idx / (D / 8);
-            const int col = (idx % (D / 8)) * 8;
-            *reinterpret_cast<u32x4*>(&sm.k[buf][key * Smem<D>::kStride + col]) = kr[c];
-            *reinterpret_cast<u32x4*>(&sm.v[buf][key * Smem<D>::vStride + col]) = vr[c];
+            *reinterpret_cast<u32x4*>(&tile[(idx / (D / 8)) * stride + (idx % (D / 8)) * 8]) = r[c];
         }
     }
 };
@@ -122,10 +125,116 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_u16*)(p));
 }
 
+// Per-wavefront state of the key loop and the three phases of one key tile.
+template <int D, bool CAUSAL>
+struct Wave {
+    static constexpr int KS = D / 16;  // k-steps of Q K^T
+    static constexpr int DB = D / 32;  // 32-wide blocks of the output dimension
+
+    bf16x8 qf[KS];   // Q^T fragments (B operand of S^T = K Q^T)
+    f32x16 acc[DB];  // O^T accumulator: this lane's query row, 16 of each 32 outputs
+    float m;         // reference max of |scale| log2(e) score, this lane's row (see kLazy)
+    float l;         // running partial sum over this lane's half of every tile
+    float c;         // |scale| log2(e)
+    int half, l32, k_off, v_off, my_q, key_lim;
+
+    // S^T = K Q^T for the two 32-key halves of a tile (A = K rows from LDS).
+    __device__ __forceinline__ void qk(f32x16 (&st)[2], const uint16_t* ktile) const {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            f32x16 a = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+                    ktile + k_off + 32 * sb * Smem<D>::kStride + 16 * ks);
+                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], a, 0, 0, 0);
+            }
+            st[sb] = a;
+        }
+    }
+
+    // Online-softmax update of one tile: hidden keys (diagonal / ragged tiles only)
+    // take no part; on return st holds P = exp2(c s - m_new) and the running state is
+    // updated.  Returns alpha = exp2(m_old - m_new), exactly 1 when the reference
+    // maximum stays.
+    template <bool MASK>
+    __device__ __forceinline__ float softmax(f32x16 (&st)[2], int j0) {
+        if (MASK) {
+            const int key0 = j0 + 4 * half;  // key of st[0][0]
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = key0 + 32 * sb + 8 * (r >> 2) + (r & 3);
+                    st[sb][r] = key <= key_lim ? st[sb][r] : kNegInf;
+                }
+        }
+        float mt = kNegInf;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[sb][r]);
+        mt = fmaxf(mt, swap_halves(mt)) * c;
+        // m = -inf (nothing seen yet) always moves: -inf + kLazy is -inf
+        const float m_new = mt > m + kLazy ? mt : m;
+        const float base = safe_base(m_new);
+        const float alpha = fast_exp2(m - base);  // 1 when m stays; 0 when m = -inf
+        float ps = 0.0f;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float e = fast_exp2(fmaf(st[sb][r], c, -base));
+                // exactly 0 for hidden keys (exp2 of c * -inf is NaN when c = 0)
+                if (MASK) e = st[sb][r] == kNegInf ? 0.0f : e;
+                st[sb][r] = e;
+                ps += e;
+            }
+        l = alpha * l + ps;
+        m = m_new;
+        return alpha;
+    }
+
+    // O^T = alpha O^T + V^T P^T.  A operand for output rows 32 b .. 32 b + 31 and key
+    // group g: lane l needs V[16 g + 4 half + t][32 b + l32] (t = 0..3) and
+    // V[16 g + 8 + 4 half + t][32 b + l32], read transposed from row-major V.
+    __device__ __forceinline__ void pv(const f32x16 (&pt)[2], float alpha, const uint16_t* vtile) {
+        if (__ballot(alpha != 1.0f) != 0) {  // skipped when no running max moved
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+        }
+        bf16x8 pf[4];  // P^T fragments: this lane's values 8 hb .. 8 hb + 7 of each half
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                u32x4 w;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    w[t] = pack_bf16x2(pt[sb][8 * hb + 2 * t], pt[sb][8 * hb + 2 * t + 1]);
+                pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
+            }
+        const uint16_t* vb = vtile + v_off;
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const uint16_t* pa = vb + 16 * g * Smem<D>::vStride + 32 * b;
+                const i16x4 lo = lds_read_tr16(pa);
+                const i16x4 hi = lds_read_tr16(pa + 8 * Smem<D>::vStride);
+                const bf16x8 a =
+                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], acc[b], 0, 0, 0);
+            }
+    }
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
-    constexpr int KS = D / 16;  // k-steps of Q K^T
-    constexpr int DB = D / 32;  // 32-wide blocks of the output dimension
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
     __shared__ Smem<D> sm;
 
     // XCD-aware remap: block id b runs on XCD b % 8; give each XCD a contiguous
@@ -141,171 +250,125 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int l32 = lane & 31;
-    const int half = lane >> 5;
-    // Lane's block for the transposing V reads: row 4 half + (lane % 16) / 4 of the
-    // key group, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of the output block.
-    const int v_lane_off = (4 * half + ((lane & 15) >> 2)) * Smem<D>::vStride +
-                           16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const int64_t head = (int64_t)bh * N * D;
     const uint16_t* kh = p.k + head;
     const uint16_t* vh = p.v + head;
 
     const int q0 = qt * kBM;
-    const int qw0 = q0 + 32 * wave;          // this wavefront's first query row
-    const int my_q = qw0 + l32;              // the query row this lane owns
+    const int qw0 = q0 + 32 * wave;  // this wavefront's first query row
     const int qw_last = min(qw0 + 31, N - 1);
     const bool wave_live = qw0 < N;
 
-    // Q^T fragments (B operand): lane supplies Q[my_q][16 s + 8 half + 0..7].
-    // With a negative scale the query is negated (exact in bf16) and |scale| used, so
-    // the row maximum of the raw products is the maximum of the scaled scores.
-    bf16x8 qf[KS];
+    Wave<D, CAUSAL> w;
+    w.l32 = lane & 31;
+    w.half = lane >> 5;
+    w.my_q = qw0 + w.l32;
+    w.key_lim = CAUSAL ? min(N - 1, w.my_q) : N - 1;  // last visible key of the row
+    w.c = p.scale_log2;
+    w.m = kNegInf;
+    w.l = 0.0f;
+    // K fragment of lane l: row l32 (+32 sb) of the tile, columns 16 ks + 8 half.
+    w.k_off = w.l32 * Smem<D>::kStride + 8 * w.half;
+    // Lane's block for the transposing V reads: row 4 half + (lane % 16) / 4 of the
+    // key group, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of the output block.
+    w.v_off = (4 * w.half + ((lane & 15) >> 2)) * Smem<D>::vStride + 16 * ((lane >> 4) & 1) +
+              4 * (lane & 3);
+
+    // Q^T fragments: lane supplies Q[my_q][16 s + 8 half + 0..7].  With a negative
+    // scale the query is negated (exact in bf16) and |scale| used, so the row maximum
+    // of the raw products is the maximum of the scaled scores.
     const uint32_t qsign = p.negate_q ? 0x80008000u : 0u;
-    const int q_row = min(my_q, N - 1);  // rows past the end compute garbage, never stored
+    const int q_row = min(w.my_q, N - 1);  // rows past the end compute garbage, never stored
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p.q + head + (int64_t)q_row * D + 16 * s + 8 * half);
-        qf[s] = __builtin_bit_cast(bf16x8, w ^ qsign);
+        const u32x4 v4 =
+            *reinterpret_cast<const u32x4*>(p.q + head + (int64_t)q_row * D + 16 * s + 8 * w.half);
+        w.qf[s] = __builtin_bit_cast(bf16x8, v4 ^ qsign);
     }
-
-    f32x16 acc[DB];
 #pragma unroll
-    for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
-    float m = kNegInf;  // running max of scale * log2e * score, this lane's row
-    float l = 0.0f;     // running partial sum over this lane's half of each tile
+    for (int b = 0; b < DB; ++b) w.acc[b] = f32x16{};
 
     const int q_last = min(q0 + kBM - 1, N - 1);
     const int n_kv = CAUSAL ? (q_last / kBN + 1) : (N + kBN - 1) / kBN;
 
-    Stage<D> stage;
-    stage.load(kh, vh, 0, N, tid);
-    stage.store(sm, 0, tid);
-    __syncthreads();
-
-    for (int j = 0; j < n_kv; ++j) {
-        const int buf = j & 1;
-        const int j0 = j * kBN;
-        if (j + 1 < n_kv) stage.load(kh, vh, j0 + kBN, N, tid);
-
-        const bool active = wave_live && (!CAUSAL || j0 <= qw_last);
-        if (active) {
-            // ---- S^T = K Q^T for the two 32-key halves of the tile
-            f32x16 s[2] = {f32x16{}, f32x16{}};
-            const uint16_t* kb = &sm.k[buf][0];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        kb + (32 * sb + l32) * Smem<D>::kStride + 16 * ks + 8 * half);
-                    s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
-                }
-            }
-
-            // ---- row max of the raw products (scale >= 0 after the sign flip of Q);
-            // on diagonal / ragged tiles hidden keys take no part.
-            const bool need_mask = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
-            int key_lim = N - 1;  // last visible key of this lane's row
-            if (CAUSAL) key_lim = min(key_lim, my_q);
-            const int key0 = j0 + 4 * half;  // key of s[0][0]
-            float mt = kNegInf;
-            if (need_mask) {
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = key0 + 32 * sb + 8 * (r >> 2) + (r & 3);
-                        s[sb][r] = key <= key_lim ? s[sb][r] : kNegInf;
-                    }
-            }
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
-            mt = fmaxf(mt, swap_halves(mt));
-            // m is kept in log2 units of the scaled score: c * max(raw), c = |scale| log2 e
-            const float m_new = fmaxf(m, mt * p.scale_log2);
-            const float base = safe_base(m_new);
-            const float alpha = fast_exp2(m - base);  // m = -inf gives 0
-
-            // ---- P = exp2(c s - m_new) with one FMA per score, partial row sums.
-            // Hidden keys get exactly 0 (not exp2 of c * -inf, which is NaN at c = 0).
-            float ps = 0.0f;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float e = fast_exp2(fmaf(s[sb][r], p.scale_log2, -base));
-                    if (need_mask) e = s[sb][r] == kNegInf ? 0.0f : e;
-                    s[sb][r] = e;
-                    ps += e;
-                }
-            }
-            l = alpha * l + ps;
-            m = m_new;
-
-            // ---- rescale O (skipped when no running max moved: alpha == 1 exactly)
-            if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
-            }
-
-            // ---- P^T fragments: lane's values 8 hb .. 8 hb + 7 of each half-tile
-            bf16x8 pf[4];
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb) {
-                    u32x4 w;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        w[t] = pack_bf16x2(s[sb][8 * hb + 2 * t], s[sb][8 * hb + 2 * t + 1]);
-                    pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
-                }
-            }
-
-            // ---- O^T += V^T P^T.  A operand for output rows 32 b .. 32 b + 31 and key
-            // group g: lane l needs V[16 g + 4 half + t][32 b + l32] (t = 0..3) and
-            // V[16 g + 8 + 4 half + t][32 b + l32]; each lane of a 16-lane group
-            // points at one 4-element block of those rows (see v_lane_off).
-            const uint16_t* vb = &sm.v[buf][v_lane_off];
-#pragma unroll
-            for (int b = 0; b < DB; ++b) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint16_t* pa = vb + 16 * g * Smem<D>::vStride + 32 * b;
-                    const i16x4 lo = lds_read_tr16(pa);
-                    const i16x4 hi = lds_read_tr16(pa + 8 * Smem<D>::vStride);
-                    const bf16x8 a = __builtin_bit_cast(
-                        bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], acc[b], 0, 0, 0);
-                }
-            }
-        }
-
-        if (j + 1 < n_kv) stage.store(sm, buf ^ 1, tid);
-        __syncthreads();
+    // Software pipeline over key tiles.  Iteration j reads K_{j+1} (scores of the next
+    // tile, on the matrix cores) and V_j (output of this tile), while the vector ALUs
+    // run the softmax of tile j; meanwhile K_{j+2} and V_{j+1} travel from HBM to
+    // registers and are written to the buffers that iteration j-1 finished reading.
+    // K is therefore one tile ahead of V; one barrier per tile orders it all.
+    Prefetch<D> kpf, vpf;
+    kpf.load(kh, 0, N, tid);
+    vpf.load(vh, 0, N, tid);
+    kpf.store(sm.k[0], Smem<D>::kStride, tid);
+    vpf.store(sm.v[0], Smem<D>::vStride, tid);
+    if (n_kv > 1) {
+        kpf.load(kh, kBN, N, tid);
+        kpf.store(sm.k[1], Smem<D>::kStride, tid);
     }
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    if (wave_live) w.qk(sa, sm.k[0]);
+    __syncthreads();  // K buffer 0 may now be refilled
+
+    auto step = [&](int j, f32x16(&sc)[2], f32x16(&sn)[2]) {
+        const int j0 = j * kBN;
+        const bool has_next = j + 1 < n_kv;
+        const bool act_cur = wave_live && (!CAUSAL || j0 <= qw_last);
+        const bool act_next = wave_live && has_next && (!CAUSAL || j0 + kBN <= qw_last);
+        const bool pf_k = j + 2 < n_kv;
+        if (pf_k) kpf.load(kh, j0 + 2 * kBN, N, tid);
+        if (has_next) vpf.load(vh, j0 + kBN, N, tid);
+        const bool mask_cur = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
+        const uint16_t* kn = sm.k[(j + 1) & 1];
+        float alpha = 1.0f;
+        if (act_cur && act_next && !mask_cur) {
+            // steady state: next tile's scores and this tile's softmax in one block
+            w.qk(sn, kn);
+            alpha = w.template softmax<false>(sc, j0);
+            // Interleave: each of the 16 matrix instructions (32 cycles on the matrix
+            // core) is followed by a run of the softmax's vector instructions, which
+            // do not depend on it, so both units stay busy.
+            // K fragments are read two matrix instructions ahead of their use.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads (K fragments)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // vector ALU
+            }
+        } else {
+            if (act_next) w.qk(sn, kn);
+            if (act_cur) alpha = mask_cur ? w.template softmax<true>(sc, j0) : w.template softmax<false>(sc, j0);
+        }
+        if (act_cur) w.pv(sc, alpha, sm.v[j & 1]);
+        if (pf_k) kpf.store(sm.k[j & 1], Smem<D>::kStride, tid);
+        if (has_next) vpf.store(sm.v[(j + 1) & 1], Smem<D>::vStride, tid);
+        __syncthreads();
+    };
+
+    int j = 0;
+    for (; j + 1 < n_kv; j += 2) {
+        step(j, sa, sb);
+        step(j + 1, sb, sa);
+    }
+    if (j < n_kv) step(j, sa, sb);
 
     if (!wave_live) return;
-    const float l_row = l + swap_halves(l);
-    if (my_q < N) {
+    const float l_row = w.l + swap_halves(w.l);
+    if (w.my_q < N) {
         const float inv = 1.0f / l_row;
-        uint16_t* orow = p.o + head + (int64_t)my_q * D;
+        uint16_t* orow = p.o + head + (int64_t)w.my_q * D;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                u32x2 w;
-                w[0] = pack_bf16x2(acc[b][4 * i + 0] * inv, acc[b][4 * i + 1] * inv);
-                w[1] = pack_bf16x2(acc[b][4 * i + 2] * inv, acc[b][4 * i + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * i + 4 * half) = w;
+                u32x2 o2;
+                o2[0] = pack_bf16x2(w.acc[b][4 * i + 0] * inv, w.acc[b][4 * i + 1] * inv);
+                o2[1] = pack_bf16x2(w.acc[b][4 * i + 2] * inv, w.acc[b][4 * i + 3] * inv);
+                *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * i + 4 * w.half) = o2;
             }
         }
-        if (half == 0) p.lse[(int64_t)bh * N + my_q] = (m + fast_log2(l_row)) * kLn2;
+        if (w.half == 0) p.lse[(int64_t)bh * N + w.my_q] = (w.m + fast_log2(l_row)) * kLn2;
     }
 }
 
