@@ -2,7 +2,7 @@
 //
 // Algorithm: "Softmax numerical stability and IO-aware attention" (zhouzhq2021.github.io),
 // section 7: per query tile, initialise m = -inf, l = 0, O = 0; for every key/value
-// tile form S = Q K^T, m_new = max(m, rowmax S), P = exp(S - m_new),
+// tile form S = Q K^T, take the new row maximum, P = exp(S - m_new),
 // alpha = exp(m - m_new), l = alpha l + rowsum P, O = alpha O + P V; finally O / l.
 // Section 8 (FlashAttention-2) adds the choices kept here: the query tile is the outer
 // loop so O is written once, the division by l is deferred to the end, and key tiles
@@ -11,7 +11,7 @@
 // gfx950 mapping (a design of its own, not the pages' warp/shared-memory scheme):
 //
 //   * Block = 4 wavefronts = 128 query rows; each wavefront owns 32 query rows for
-//     the whole key loop.  Key tiles are 64 keys, double-buffered in LDS.
+//     the whole key loop.  Key tiles are 64 keys.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     A = a 32-key slice of K (from LDS), B = Q^T (held in registers for the whole
 //     loop).  In the 32x32 accumulator, lane l holds one column, i.e. one query row
@@ -20,24 +20,33 @@
 //     exchange at all until the end (each half keeps a partial l under the same m).
 //   * The output is accumulated transposed too, O^T += V^T P^T: the B operand
 //     (P^T, 8 keys x 1 query per lane) is exactly what the lane already holds after
-//     the exponentials, converted to bf16 with no data movement.  V is staged in LDS
-//     row-major, exactly like K, and the A operand (V^T) is read with the gfx950
-//     transposing LDS load ds_read_b64_tr_b16: two of them give a lane the 8 keys
-//     (4h..4h+3 and 8+4h..8+4h+3 of a 16-key group) of its output column, the order
-//     in which the S^T accumulator hands P to the lanes.  The O^T accumulator keeps
-//     one query row per lane as well, so alpha rescales it with no exchange.
-//   * LDS row strides: K rows are D*2+16 bytes and V rows D*2+64 bytes, the paddings
-//     under which the 16-byte K reads and the transposing V reads are free of bank
-//     conflicts on gfx950's LDS.
+//     the exponentials, converted to bf16 with no data movement.  V is kept in LDS
+//     row-major and the A operand (V^T) is read with the gfx950 transposing LDS load
+//     ds_read_b64_tr_b16: two of them give a lane the 8 keys (4h..4h+3 and
+//     8+4h..8+4h+3 of a 16-key group) of its output column, the order in which the
+//     S^T accumulator hands P to the lanes.  The O^T accumulator keeps one query row
+//     per lane as well, so alpha rescales it with no exchange.
+//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4: each lane's
+//     16 bytes land at base + 16 * lane), with no registers and no LDS write
+//     instructions.  The rows are unpadded and each row's 16-byte chunks are stored
+//     XOR-permuted, a permutation chosen so that the 16-byte K reads and the
+//     transposing V reads are free of LDS bank conflicts; a lane fetches the chunk
+//     that belongs at its LDS position.
+//   * Software pipeline, three tiles deep: while the matrix cores compute O += P V of
+//     the previous tile and then S of the next tile, the vector ALUs run this tile's
+//     softmax, interleaved instruction by instruction (sched_group_barrier).
 //   * The row's reference maximum m moves lazily: only when a tile's maximum exceeds
 //     it by more than 2^8 (kLazy).  Until then alpha is exactly 1 and the rescale of O
 //     is skipped (decided per wavefront); P stays at most 2^8.  The result O / l and
 //     LSE = m + ln l do not depend on which reference m is used.
-//   * Exponentials use the hardware exp2 on scores pre-multiplied by scale * log2 e.
+//   * Exponentials use the hardware exp2 on |scale| log2(e) s - m (one FMA per score);
+//     a negative scale negates Q, which is exact.
 //   * Block ids are remapped so each of the 8 XCDs (which receive block ids round
 //     robin) walks a contiguous range of (head, query tile) pairs: the key/value
 //     stream of a head is then shared through that XCD's L2.  In causal mode the
 //     tiles of a head run longest-first.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 
@@ -48,18 +57,15 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per block
 constexpr int kBN = 64;           // keys per tile
-
-template <int D>
-struct Smem {
-    static constexpr int kStride = D + 8;    // bf16 per K row
-    static constexpr int vStride = D + 32;   // bf16 per V row
-    uint16_t k[2][kBN * kStride];
-    uint16_t v[2][kBN * vStride];
-};
 
 // Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -74,6 +80,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // is skipped.  O / l and LSE = m + log l are the same for any reference m.
 constexpr float kLazy = 8.0f;
 
+// LDS layout of one 64 x D tile: rows of D bf16 (RB bytes), 16-byte chunk c of row r
+// stored at chunk position c ^ swz(r).
+template <int D>
+struct Layout {
+    static constexpr int RB = 2 * D;            // bytes per row
+    static constexpr int NCH = RB / 16;         // 16-byte chunks per row
+    static constexpr int TILE = kBN * RB;       // bytes per tile
+    static constexpr int ROUNDS = TILE / 4096;  // 16-byte copies per thread per tile
+    static constexpr int ROWS_PER_ROUND = 4096 / RB;
+    // K is read as 16-byte fragments by 32 lanes on 32 consecutive rows.
+    __device__ static constexpr int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+    // V is read with the transposing 8-byte load on 8 consecutive rows x 4 chunks.
+    // Both stay below NCH, so a permuted chunk never leaves its row.
+    __device__ static constexpr int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 2 * (r & 3); }
+};
+
 struct Params {
     const uint16_t* q;
     const uint16_t* k;
@@ -87,78 +109,79 @@ struct Params {
     int negate_q;      // scale < 0
 };
 
-// Global -> register -> LDS staging of one 64-key tile of K or V (64 x D, row-major),
-// 16 bytes per access: consecutive threads take consecutive 16-byte chunks of a row,
-// so global reads are fully coalesced and LDS writes are free of bank conflicts.
-template <int D>
-struct Prefetch {
-    static constexpr int kChunks = kBN * D / 8 / 256;  // 16-byte chunks per thread
-    u32x4 r[kChunks];
-
-    __device__ __forceinline__ void load(const uint16_t* base, int j0, int N, int tid) {
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            const int idx = tid + 256 * c;
-            // Rows past the end re-read row N-1: their scores are masked to -inf and
-            // their probabilities are 0, so any finite content will do.
-            const int key = min(j0 + idx / (D / 8), N - 1);
-            r[c] = *reinterpret_cast<const u32x4*>(base + (int64_t)key * D + (idx % (D / 8)) * 8);
-        }
-    }
-
-    __device__ __forceinline__ void store(uint16_t* tile, int stride, int tid) const {
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            const int idx = tid + 256 * c;
-            *reinterpret_cast<u32x4*>(&tile[(idx / (D / 8)) * stride + (idx % (D / 8)) * 8]) = r[c];
-        }
-    }
-};
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
 // Transposing LDS load: within each group of 16 lanes, lane i receives element i % 4
 // of the 8-byte blocks addressed by lanes i / 4 + 4 k, k = 0..3.
-__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
-    typedef __attribute__((address_space(3))) uint16_t lds_u16;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_u16*)(p));
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const lds_char*)(p));
 }
 
-// Per-wavefront state of the key loop and the three phases of one key tile.
+// One tile of K or V from HBM straight to LDS.  Thread t writes LDS bytes
+// 4096 * round + 16 * t, i.e. row ROWS_PER_ROUND * round + t / NCH at chunk position
+// t % NCH, so it fetches logical chunk (t % NCH) ^ swz(row) of that row.  `src_off`
+// is that per-thread byte offset within a round (the same for every round and tile,
+// because the swizzles repeat every ROWS_PER_ROUND rows); `src_col` is its column
+// part.  Rows at or past N (only in the last tile) re-read row N-1: their scores are
+// masked and their probabilities are 0, so any finite content will do.
+template <int D>
+__device__ __forceinline__ void tile_to_lds(char* lds_tile, const char* head, int j0, int N, int tid,
+                                            int src_off, int src_col) {
+    using L = Layout<D>;
+    char* dst = lds_tile + 1024 * (tid >> 6);  // wave-uniform; the lane offset is implicit
+    if (j0 + kBN <= N) {
+#pragma unroll
+        for (int r = 0; r < L::ROUNDS; ++r) {
+            const char* src = head + (int64_t)(j0 + L::ROWS_PER_ROUND * r) * L::RB + src_off;
+            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 4096 * r), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < L::ROUNDS; ++r) {
+            const int row = min(j0 + L::ROWS_PER_ROUND * r + tid / L::NCH, N - 1);
+            const char* src = head + (int64_t)row * L::RB + src_col;
+            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 4096 * r), 16, 0, 0);
+        }
+    }
+}
+
+// Per-wavefront state of the key loop and the phases of one key tile.
 template <int D, bool CAUSAL>
 struct Wave {
+    using L = Layout<D>;
     static constexpr int KS = D / 16;  // k-steps of Q K^T
     static constexpr int DB = D / 32;  // 32-wide blocks of the output dimension
 
     bf16x8 qf[KS];   // Q^T fragments (B operand of S^T = K Q^T)
     f32x16 acc[DB];  // O^T accumulator: this lane's query row, 16 of each 32 outputs
+    bf16x8 pf[4];    // P^T fragments of the last finished tile (B operand of O^T += V^T P^T)
+    int k_off[KS];   // byte offset of this lane's K fragment for k-step ks (row l32)
+    int v_off[DB];   // byte offset of this lane's transposing V block for output block b
     float m;         // reference max of |scale| log2(e) score, this lane's row (see kLazy)
     float l;         // running partial sum over this lane's half of every tile
     float c;         // |scale| log2(e)
-    int half, l32, k_off, v_off, my_q, key_lim;
+    float base;      // finite stand-in for m while a tile is exponentiated
+    float alpha;     // exp2(m_old - m_new) of the tile in flight
+    float ps;        // partial row sum of the tile in flight
+    int half, key_lim;
 
     // S^T = K Q^T for the two 32-key halves of a tile (A = K rows from LDS).
-    __device__ __forceinline__ void qk(f32x16 (&st)[2], const uint16_t* ktile) const {
+    __device__ __forceinline__ void qk(f32x16 (&st)[2], const char* ktile) const {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             f32x16 a = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-                    ktile + k_off + 32 * sb * Smem<D>::kStride + 16 * ks);
+                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ktile + 32 * sb * L::RB + k_off[ks]);
                 a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], a, 0, 0, 0);
             }
             st[sb] = a;
         }
     }
 
-    // Online-softmax update of one tile: hidden keys (diagonal / ragged tiles only)
-    // take no part; on return st holds P = exp2(c s - m_new) and the running state is
-    // updated.  Returns alpha = exp2(m_old - m_new), exactly 1 when the reference
-    // maximum stays.
+    // First half of the online-softmax update of a tile: hidden keys (diagonal /
+    // ragged tiles only) take no part; the row maximum moves the reference m if it
+    // exceeds it by more than kLazy; the first 32-key half is exponentiated in place.
     template <bool MASK>
-    __device__ __forceinline__ float softmax(f32x16 (&st)[2], int j0) {
+    __device__ __forceinline__ void softmax_a(f32x16 (&st)[2], int j0) {
         if (MASK) {
             const int key0 = j0 + 4 * half;  // key of st[0][0]
 #pragma unroll
@@ -177,35 +200,18 @@ struct Wave {
         mt = fmaxf(mt, swap_halves(mt)) * c;
         // m = -inf (nothing seen yet) always moves: -inf + kLazy is -inf
         const float m_new = mt > m + kLazy ? mt : m;
-        const float base = safe_base(m_new);
-        const float alpha = fast_exp2(m - base);  // 1 when m stays; 0 when m = -inf
-        float ps = 0.0f;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float e = fast_exp2(fmaf(st[sb][r], c, -base));
-                // exactly 0 for hidden keys (exp2 of c * -inf is NaN when c = 0)
-                if (MASK) e = st[sb][r] == kNegInf ? 0.0f : e;
-                st[sb][r] = e;
-                ps += e;
-            }
-        l = alpha * l + ps;
+        base = safe_base(m_new);
+        alpha = fast_exp2(m - base);  // 1 when m stays; 0 when m = -inf
         m = m_new;
-        return alpha;
+        ps = 0.0f;
+        exp_half<MASK>(st[0]);
     }
 
-    // O^T = alpha O^T + V^T P^T.  A operand for output rows 32 b .. 32 b + 31 and key
-    // group g: lane l needs V[16 g + 4 half + t][32 b + l32] (t = 0..3) and
-    // V[16 g + 8 + 4 half + t][32 b + l32], read transposed from row-major V.
-    __device__ __forceinline__ void pv(const f32x16 (&pt)[2], float alpha, const uint16_t* vtile) {
-        if (__ballot(alpha != 1.0f) != 0) {  // skipped when no running max moved
-#pragma unroll
-            for (int b = 0; b < DB; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
-        }
-        bf16x8 pf[4];  // P^T fragments: this lane's values 8 hb .. 8 hb + 7 of each half
+    // Second half: exponentiate the other 32 keys, update l, and pack P^T to bf16.
+    template <bool MASK>
+    __device__ __forceinline__ void softmax_b(f32x16 (&st)[2]) {
+        exp_half<MASK>(st[1]);
+        l = alpha * l + ps;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -213,17 +219,46 @@ struct Wave {
                 u32x4 w;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    w[t] = pack_bf16x2(pt[sb][8 * hb + 2 * t], pt[sb][8 * hb + 2 * t + 1]);
+                    w[t] = pack_bf16x2(st[sb][8 * hb + 2 * t], st[sb][8 * hb + 2 * t + 1]);
                 pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
             }
-        const uint16_t* vb = vtile + v_off;
+    }
+
+    template <bool MASK>
+    __device__ __forceinline__ void exp_half(f32x16& x) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float e = fast_exp2(fmaf(x[r], c, -base));
+            // exactly 0 for hidden keys (exp2 of c * -inf is NaN when c = 0)
+            if (MASK) e = x[r] == kNegInf ? 0.0f : e;
+            x[r] = e;
+            ps += e;
+        }
+    }
+
+    // O^T *= alpha, skipped (per wavefront) when no row moved its reference maximum.
+    __device__ __forceinline__ void rescale() {
+        if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+        }
+    }
+
+    // O^T += V^T P^T with the packed P of the last finished tile.  A operand for
+    // output rows 32 b .. 32 b + 31 and key group g: lane l needs
+    // V[16 g + 4 half + t][32 b + l32] (t = 0..3) and V[16 g + 8 + 4 half + t][32 b + l32],
+    // read transposed from row-major V.  Rows 16 g and 16 g + 8 are multiples of 8, so
+    // the swizzle (a function of the row mod 4 or mod 8) is already in v_off.
+    __device__ __forceinline__ void pv(const char* vtile) {
 #pragma unroll
         for (int b = 0; b < DB; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const uint16_t* pa = vb + 16 * g * Smem<D>::vStride + 32 * b;
+                const char* pa = vtile + 16 * g * L::RB + v_off[b];
                 const i16x4 lo = lds_read_tr16(pa);
-                const i16x4 hi = lds_read_tr16(pa + 8 * Smem<D>::vStride);
+                const i16x4 hi = lds_read_tr16(pa + 8 * L::RB);
                 const bf16x8 a =
                     __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], acc[b], 0, 0, 0);
@@ -233,9 +268,15 @@ struct Wave {
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
+    using L = Layout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    __shared__ Smem<D> sm;
+    // Two K and two V tile buffers, as separate objects so that the compiler can tell
+    // the buffer being filled from the one being read.
+    __shared__ __attribute__((aligned(1024))) char k_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[L::TILE];
 
     // XCD-aware remap: block id b runs on XCD b % 8; give each XCD a contiguous
     // range of logical ids.
@@ -251,34 +292,47 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int64_t head = (int64_t)bh * N * D;
-    const uint16_t* kh = p.k + head;
-    const uint16_t* vh = p.v + head;
+    const char* kh = reinterpret_cast<const char*>(p.k + head);
+    const char* vh = reinterpret_cast<const char*>(p.v + head);
 
     const int q0 = qt * kBM;
     const int qw0 = q0 + 32 * wave;  // this wavefront's first query row
-    const int qw_last = min(qw0 + 31, N - 1);
     const bool wave_live = qw0 < N;
 
+    // Per-thread source offsets of the HBM -> LDS copies (see tile_to_lds).
+    const int t_row = tid / L::NCH, t_pos = tid % L::NCH;
+    const int k_src_col = 16 * (t_pos ^ L::k_swz(t_row));
+    const int v_src_col = 16 * (t_pos ^ L::v_swz(t_row));
+    const int k_src = t_row * L::RB + k_src_col;
+    const int v_src = t_row * L::RB + v_src_col;
+
     Wave<D, CAUSAL> w;
-    w.l32 = lane & 31;
+    const int l32 = lane & 31;
     w.half = lane >> 5;
-    w.my_q = qw0 + w.l32;
-    w.key_lim = CAUSAL ? min(N - 1, w.my_q) : N - 1;  // last visible key of the row
+    const int my_q = qw0 + l32;
+    w.key_lim = CAUSAL ? min(N - 1, my_q) : N - 1;  // last visible key of the row
     w.c = p.scale_log2;
     w.m = kNegInf;
     w.l = 0.0f;
-    // K fragment of lane l: row l32 (+32 sb) of the tile, columns 16 ks + 8 half.
-    w.k_off = w.l32 * Smem<D>::kStride + 8 * w.half;
-    // Lane's block for the transposing V reads: row 4 half + (lane % 16) / 4 of the
-    // key group, columns 16 ((lane / 16) % 2) + 4 (lane % 4) of the output block.
-    w.v_off = (4 * w.half + ((lane & 15) >> 2)) * Smem<D>::vStride + 16 * ((lane >> 4) & 1) +
-              4 * (lane & 3);
+    // K fragment of lane l: row l32 (+32 sb) of the tile, logical chunk 2 ks + half.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w.k_off[ks] = l32 * L::RB + 16 * ((2 * ks + w.half) ^ L::k_swz(l32));
+    // Transposing V block of lane l: row 4 half + (lane % 16) / 4 of the key group,
+    // byte column 64 b + 32 ((lane / 16) % 2) + 8 (lane % 4) of the output block.
+    {
+        const int vr = 4 * w.half + ((lane & 15) >> 2);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const int col = 64 * b + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+            w.v_off[b] = vr * L::RB + 16 * ((col >> 4) ^ L::v_swz(vr)) + (col & 15);
+        }
+    }
 
     // Q^T fragments: lane supplies Q[my_q][16 s + 8 half + 0..7].  With a negative
     // scale the query is negated (exact in bf16) and |scale| used, so the row maximum
     // of the raw products is the maximum of the scaled scores.
     const uint32_t qsign = p.negate_q ? 0x80008000u : 0u;
-    const int q_row = min(w.my_q, N - 1);  // rows past the end compute garbage, never stored
+    const int q_row = min(my_q, N - 1);  // rows past the end compute garbage, never stored
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         const u32x4 v4 =
@@ -289,75 +343,97 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     for (int b = 0; b < DB; ++b) w.acc[b] = f32x16{};
 
     const int q_last = min(q0 + kBM - 1, N - 1);
-    const int n_kv = CAUSAL ? (q_last / kBN + 1) : (N + kBN - 1) / kBN;
+    const int n_kv = CAUSAL ? (q_last / kBN + 1) : (N + kBN - 1) / kBN;  // tiles of the block
+    // tiles this wavefront needs (a prefix of the block's tiles)
+    const int n_w = !wave_live ? 0 : CAUSAL ? min(n_kv, min(qw0 + 31, N - 1) / kBN + 1) : n_kv;
 
-    // Software pipeline over key tiles.  Iteration j reads K_{j+1} (scores of the next
-    // tile, on the matrix cores) and V_j (output of this tile), while the vector ALUs
-    // run the softmax of tile j; meanwhile K_{j+2} and V_{j+1} travel from HBM to
-    // registers and are written to the buffers that iteration j-1 finished reading.
-    // K is therefore one tile ahead of V; one barrier per tile orders it all.
-    Prefetch<D> kpf, vpf;
-    kpf.load(kh, 0, N, tid);
-    vpf.load(vh, 0, N, tid);
-    kpf.store(sm.k[0], Smem<D>::kStride, tid);
-    vpf.store(sm.v[0], Smem<D>::vStride, tid);
-    if (n_kv > 1) {
-        kpf.load(kh, kBN, N, tid);
-        kpf.store(sm.k[1], Smem<D>::kStride, tid);
-    }
+    // Software pipeline over key tiles, three tiles deep.  Iteration j:
+    //   phase A: O += P_{j-1} V_{j-1} on the matrix cores, while the vector ALUs take
+    //            the row maximum of S_j and exponentiate its first half;
+    //   phase B: S_{j+1} = K_{j+1} Q^T on the matrix cores, while the vector ALUs
+    //            finish P_j and pack it to bf16;
+    //   then O *= alpha_j (rarely needed).  K_{j+2} and V_j travel from HBM to the LDS
+    //   buffers that iteration j-1 finished reading, during the iteration.
+    // K is two tiles ahead of V; one barrier per tile orders everything.
+    tile_to_lds<D>(k_lds0, kh, 0, N, tid, k_src, k_src_col);
+    if (n_kv > 1) tile_to_lds<D>(k_lds1, kh, kBN, N, tid, k_src, k_src_col);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies have landed
     __syncthreads();
     f32x16 sa[2], sb[2];
-    if (wave_live) w.qk(sa, sm.k[0]);
+    if (n_w > 0) w.qk(sa, k_lds0);
     __syncthreads();  // K buffer 0 may now be refilled
 
-    auto step = [&](int j, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    // PAR = j % 2 at compile time, so every buffer access names one LDS object.
+    auto step = [&](auto par, int j, f32x16(&sc)[2], f32x16(&sn)[2]) {
+        constexpr int PAR = decltype(par)::value;
+        char* k_fill = PAR ? k_lds1 : k_lds0;       // gets K_{j+2}
+        char* v_fill = PAR ? v_lds1 : v_lds0;       // gets V_j
+        const char* knext = PAR ? k_lds0 : k_lds1;  // holds K_{j+1}
+        const char* vprev = PAR ? v_lds0 : v_lds1;  // holds V_{j-1}
         const int j0 = j * kBN;
-        const bool has_next = j + 1 < n_kv;
-        const bool act_cur = wave_live && (!CAUSAL || j0 <= qw_last);
-        const bool act_next = wave_live && has_next && (!CAUSAL || j0 + kBN <= qw_last);
-        const bool pf_k = j + 2 < n_kv;
-        if (pf_k) kpf.load(kh, j0 + 2 * kBN, N, tid);
-        if (has_next) vpf.load(vh, j0 + kBN, N, tid);
-        const bool mask_cur = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
-        const uint16_t* kn = sm.k[(j + 1) & 1];
-        float alpha = 1.0f;
-        if (act_cur && act_next && !mask_cur) {
-            // steady state: next tile's scores and this tile's softmax in one block
-            w.qk(sn, kn);
-            alpha = w.template softmax<false>(sc, j0);
-            // Interleave: each of the 16 matrix instructions (32 cycles on the matrix
-            // core) is followed by a run of the softmax's vector instructions, which
-            // do not depend on it, so both units stay busy.
-            // K fragments are read two matrix instructions ahead of their use.
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads (K fragments)
+        const bool do_pv = j >= 1 && j - 1 < n_w;  // O += P_{j-1} V_{j-1}
+        const bool do_sm = j < n_w;                // softmax of tile j
+        const bool do_qk = j + 1 < n_w;            // S_{j+1}
+        if (j + 2 < n_kv) tile_to_lds<D>(k_fill, kh, j0 + 2 * kBN, N, tid, k_src, k_src_col);
+        tile_to_lds<D>(v_fill, vh, j0, N, tid, v_src, v_src_col);
+        const bool mask = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
+        if (do_pv && do_sm && do_qk && !mask) {
+            w.pv(vprev);
+            w.template softmax_a<false>(sc, j0);
+            // Phase A: each matrix instruction (32 cycles) is paired with two
+            // transposing V reads for a later one and a run of vector instructions.
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            }
+            w.qk(sn, knext);
+            w.template softmax_b<false>(sc);
+            // Phase B: each matrix instruction paired with one K read for a later one.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // vector ALU
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
             }
         } else {
-            if (act_next) w.qk(sn, kn);
-            if (act_cur) alpha = mask_cur ? w.template softmax<true>(sc, j0) : w.template softmax<false>(sc, j0);
+            if (do_pv) w.pv(vprev);
+            if (do_sm) {
+                if (mask)
+                    w.template softmax_a<true>(sc, j0);
+                else
+                    w.template softmax_a<false>(sc, j0);
+            }
+            if (do_qk) w.qk(sn, knext);
+            if (do_sm) {
+                if (mask)
+                    w.template softmax_b<true>(sc);
+                else
+                    w.template softmax_b<false>(sc);
+            }
         }
-        if (act_cur) w.pv(sc, alpha, sm.v[j & 1]);
-        if (pf_k) kpf.store(sm.k[j & 1], Smem<D>::kStride, tid);
-        if (has_next) vpf.store(sm.v[(j + 1) & 1], Smem<D>::vStride, tid);
+        if (do_sm) w.rescale();  // O (now holding tile j-1) *= alpha_j before P_j V_j
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's copies have landed
         __syncthreads();
     };
 
     int j = 0;
     for (; j + 1 < n_kv; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
+        step(std::integral_constant<int, 0>{}, j, sa, sb);
+        step(std::integral_constant<int, 1>{}, j + 1, sb, sa);
     }
-    if (j < n_kv) step(j, sa, sb);
+    if (j < n_kv) step(std::integral_constant<int, 0>{}, j, sa, sb);
+    // the last tile's P V (its V went to buffer (n_kv - 1) % 2)
+    if (n_w == n_kv && n_w > 0) w.pv(((n_kv - 1) & 1) ? v_lds1 : v_lds0);
 
     if (!wave_live) return;
     const float l_row = w.l + swap_halves(w.l);
-    if (w.my_q < N) {
+    if (my_q < N) {
         const float inv = 1.0f / l_row;
-        uint16_t* orow = p.o + head + (int64_t)w.my_q * D;
+        uint16_t* orow = p.o + head + (int64_t)my_q * D;
 #pragma unroll
         for (int b = 0; b < DB; ++b) {
 #pragma unroll
@@ -368,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
                 *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * i + 4 * w.half) = o2;
             }
         }
-        if (w.half == 0) p.lse[(int64_t)bh * N + w.my_q] = (w.m + fast_log2(l_row)) * kLn2;
+        if (w.half == 0) p.lse[(int64_t)bh * N + my_q] = (w.m + fast_log2(l_row)) * kLn2;
     }
 }
 
