@@ -61,7 +61,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
+
+// Word 3 of a raw (unformatted, byte-addressed) buffer resource on gfx9.
+constexpr int kBufferWord3 = 0x00020000;
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per block
@@ -117,30 +119,24 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
 
 // One tile of K or V from HBM straight to LDS.  Thread t writes LDS bytes
 // 4096 * round + 16 * t, i.e. row ROWS_PER_ROUND * round + t / NCH at chunk position
-// t % NCH, so it fetches logical chunk (t % NCH) ^ swz(row) of that row.  `src_off`
-// is that per-thread byte offset within a round (the same for every round and tile,
-// because the swizzles repeat every ROWS_PER_ROUND rows); `src_col` is its column
-// part.  Rows at or past N (only in the last tile) re-read row N-1: their scores are
-// masked and their probabilities are 0, so any finite content will do.
+// t % NCH, so it fetches logical chunk (t % NCH) ^ swz(row) of that row; `src_off` is
+// that per-thread byte offset within a round (the same for every round and tile,
+// because the swizzles repeat every ROWS_PER_ROUND rows).  The copy goes through a
+// buffer resource that spans exactly the tile's rows below N: the per-tile address
+// arithmetic is scalar, and rows at or past N (last tile only) read as zeros, whose
+// scores are masked and whose probabilities are 0.
 template <int D>
 __device__ __forceinline__ void tile_to_lds(char* lds_tile, const char* head, int j0, int N, int tid,
-                                            int src_off, int src_col) {
+                                            int src_off) {
     using L = Layout<D>;
+    const int rows = min(N - j0, kBN);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(head + (int64_t)j0 * L::RB), (short)0, rows * L::RB, kBufferWord3);
     char* dst = lds_tile + 1024 * (tid >> 6);  // wave-uniform; the lane offset is implicit
-    if (j0 + kBN <= N) {
 #pragma unroll
-        for (int r = 0; r < L::ROUNDS; ++r) {
-            const char* src = head + (int64_t)(j0 + L::ROWS_PER_ROUND * r) * L::RB + src_off;
-            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 4096 * r), 16, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < L::ROUNDS; ++r) {
-            const int row = min(j0 + L::ROWS_PER_ROUND * r + tid / L::NCH, N - 1);
-            const char* src = head + (int64_t)row * L::RB + src_col;
-            __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 4096 * r), 16, 0, 0);
-        }
-    }
+    for (int r = 0; r < L::ROUNDS; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 4096 * r), 16, src_off, 4096 * r,
+                                                 0, 0);
 }
 
 // Per-wavefront state of the key loop and the phases of one key tile.
@@ -152,7 +148,8 @@ struct Wave {
 
     bf16x8 qf[KS];   // Q^T fragments (B operand of S^T = K Q^T)
     f32x16 acc[DB];  // O^T accumulator: this lane's query row, 16 of each 32 outputs
-    bf16x8 pf[4];    // P^T fragments of the last finished tile (B operand of O^T += V^T P^T)
+    bf16x8 pf[4];    // P^T fragments of the last finished tile (B operand of O^T += V^T P^T);
+                     // a tile's new fragments are formed while P V still reads the old ones
     int k_off[KS];   // byte offset of this lane's K fragment for k-step ks (row l32)
     int v_off[DB];   // byte offset of this lane's transposing V block for output block b
     float m;         // reference max of |scale| log2(e) score, this lane's row (see kLazy)
@@ -179,7 +176,7 @@ struct Wave {
 
     // First half of the online-softmax update of a tile: hidden keys (diagonal /
     // ragged tiles only) take no part; the row maximum moves the reference m if it
-    // exceeds it by more than kLazy; the first 32-key half is exponentiated in place.
+    // exceeds it by more than kLazy; the first 32-key half is exponentiated and packed.
     template <bool MASK>
     __device__ __forceinline__ void softmax_a(f32x16 (&st)[2], int j0) {
         if (MASK) {
@@ -204,35 +201,39 @@ struct Wave {
         alpha = fast_exp2(m - base);  // 1 when m stays; 0 when m = -inf
         m = m_new;
         ps = 0.0f;
-        exp_half<MASK>(st[0]);
+        exp_half<MASK>(st[0], 0);
     }
 
-    // Second half: exponentiate the other 32 keys, update l, and pack P^T to bf16.
+    // Second half: exponentiate and pack the other 32 keys, then update l.
     template <bool MASK>
     __device__ __forceinline__ void softmax_b(f32x16 (&st)[2]) {
-        exp_half<MASK>(st[1]);
+        exp_half<MASK>(st[1], 1);
         l = alpha * l + ps;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                u32x4 w;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    w[t] = pack_bf16x2(st[sb][8 * hb + 2 * t], st[sb][8 * hb + 2 * t + 1]);
-                pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
-            }
     }
 
+    // Exponentiate 32 keys (half sb of the tile) and pack them to bf16 P^T fragments
+    // pf[2 sb], pf[2 sb + 1]; the row sum adds the packed pairs with v_dot2c_f32_bf16,
+    // so l sums exactly the weights that the P V product uses.
     template <bool MASK>
-    __device__ __forceinline__ void exp_half(f32x16& x) {
+    __device__ __forceinline__ void exp_half(f32x16& x, int sb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float e = fast_exp2(fmaf(x[r], c, -base));
             // exactly 0 for hidden keys (exp2 of c * -inf is NaN when c = 0)
             if (MASK) e = x[r] == kNegInf ? 0.0f : e;
             x[r] = e;
-            ps += e;
+        }
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            u32x4 w;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x2 pr = __builtin_convertvector(f32x2{x[8 * hb + 2 * t], x[8 * hb + 2 * t + 1]}, bf16x2);
+                ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+                w[t] = __builtin_bit_cast(uint32_t, pr);
+            }
+            pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
         }
     }
 
@@ -301,10 +302,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
 
     // Per-thread source offsets of the HBM -> LDS copies (see tile_to_lds).
     const int t_row = tid / L::NCH, t_pos = tid % L::NCH;
-    const int k_src_col = 16 * (t_pos ^ L::k_swz(t_row));
-    const int v_src_col = 16 * (t_pos ^ L::v_swz(t_row));
-    const int k_src = t_row * L::RB + k_src_col;
-    const int v_src = t_row * L::RB + v_src_col;
+    const int k_src = t_row * L::RB + 16 * (t_pos ^ L::k_swz(t_row));
+    const int v_src = t_row * L::RB + 16 * (t_pos ^ L::v_swz(t_row));
 
     Wave<D, CAUSAL> w;
     const int l32 = lane & 31;
@@ -355,8 +354,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     //   then O *= alpha_j (rarely needed).  K_{j+2} and V_j travel from HBM to the LDS
     //   buffers that iteration j-1 finished reading, during the iteration.
     // K is two tiles ahead of V; one barrier per tile orders everything.
-    tile_to_lds<D>(k_lds0, kh, 0, N, tid, k_src, k_src_col);
-    if (n_kv > 1) tile_to_lds<D>(k_lds1, kh, kBN, N, tid, k_src, k_src_col);
+    tile_to_lds<D>(k_lds0, kh, 0, N, tid, k_src);
+    if (n_kv > 1) tile_to_lds<D>(k_lds1, kh, kBN, N, tid, k_src);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies have landed
     __syncthreads();
     f32x16 sa[2], sb[2];
@@ -374,8 +373,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
         const bool do_pv = j >= 1 && j - 1 < n_w;  // O += P_{j-1} V_{j-1}
         const bool do_sm = j < n_w;                // softmax of tile j
         const bool do_qk = j + 1 < n_w;            // S_{j+1}
-        if (j + 2 < n_kv) tile_to_lds<D>(k_fill, kh, j0 + 2 * kBN, N, tid, k_src, k_src_col);
-        tile_to_lds<D>(v_fill, vh, j0, N, tid, v_src, v_src_col);
+        if (j + 2 < n_kv) tile_to_lds<D>(k_fill, kh, j0 + 2 * kBN, N, tid, k_src);
+        tile_to_lds<D>(v_fill, vh, j0, N, tid, v_src);
         const bool mask = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
         if (do_pv && do_sm && do_qk && !mask) {
             w.pv(vprev);
