@@ -40,6 +40,83 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
 
 
+CSRC = os.path.join(ROOT, "online_softmax_09_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+# kernel-name prefix in rocprofv3 output -> sources whose hash stamps its counters
+KERNEL_SOURCES = {
+    "attn_fwd_bf16": ["attn_fwd_bf16.hip", "device_common.hpp"],
+    "softmax_rows": ["softmax_rows.hip", "device_common.hpp"],
+}
+
+
+def sources_sha(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """{kernel: bytes per launch} from profiles/hbm_traffic.txt, only for kernels whose
+    sources are unchanged since the counters were taken."""
+    out = {}
+    if not os.path.exists(TRAFFIC_FILE):
+        return out
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) >= 9 and f[0] == "kernel" and f[1] in KERNEL_SOURCES:
+            rec = dict(zip(f[2::2], f[3::2]))
+            if rec.get("sources_sha256_16") == sources_sha(f[1]):
+                out[f[1]] = float(rec["fetch_bytes"]) + float(rec["write_bytes"])
+    return out
+
+
+def write_traffic(fetch_csv, write_csv, copy_mib):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) of
+    `bench.py --calib-copy-mib copy_mib` into profiles/hbm_traffic.txt.  The plain
+    device copy of known size in the same runs calibrates each counter."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * (1 << 20)
+    cf = [v for k, vs in f.items() if "copyBuffer" in k for v in vs]
+    cw = [v for k, vs in w.items() if "copyBuffer" in k for v in vs]
+    fetch_scale = copy_bytes / (np.median(cf) * 1024.0)
+    write_scale = copy_bytes / (np.median(cw) * 1024.0)
+    lines = [
+        "# HBM bytes per launch, from two rocprofv3 --pmc runs of bench.py (FETCH_SIZE, then",
+        "# WRITE_SIZE, KiB per dispatch, median over dispatches), each scaled by what the same",
+        f"# counter read for a plain {copy_mib} MiB device copy in the same run:",
+        f"#   fetch scale {fetch_scale:.4f}  write scale {write_scale:.4f}",
+        "# commands (from the repository root, one GPU):",
+        f"#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-budget 0 --calib-copy-mib {copy_mib}",
+        f"#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- python3 bench.py --steps 2 --warmup 1 --cpu-budget 0 --calib-copy-mib {copy_mib}",
+        "#   python bench.py --write-traffic <fetch csv> <write csv>",
+        "# bench.py reports a kernel's traffic only while its sources hash to sources_sha256_16.",
+    ]
+    for kern in KERNEL_SOURCES:
+        fk = [v for k, vs in f.items() if kern in k for v in vs]
+        wk = [v for k, vs in w.items() if kern in k for v in vs]
+        if not fk or not wk:
+            continue
+        lines.append(f"kernel {kern} sources_sha256_16 {sources_sha(kern)} "
+                     f"fetch_bytes {np.median(fk) * 1024.0 * fetch_scale:.0f} "
+                     f"write_bytes {np.median(wk) * 1024.0 * write_scale:.0f} "
+                     f"fetch_kib_raw {np.median(fk):.1f} write_kib_raw {np.median(wk):.1f}")
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def attn_flops(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
@@ -106,7 +183,13 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/hbm_traffic.txt from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.calib_copy_mib or 1024)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -185,6 +268,7 @@ def main():
         torch.cuda.synchronize()
 
     fl = attn_flops(B, H, N, d, causal)
+    attn_min_bytes = 2.0 * B * H * N * d * 4 + 4.0 * B * H * N  # read Q, K, V; write O; write LSE
     sm_bytes = 8.0 * cs["rows"] * cs["cols"]
     attn_avg = float(np.mean(attn_ms)) if attn_ms else float("nan")
     sm_avg = float(np.mean(sm_ms)) if sm_ms else float("nan")
@@ -202,6 +286,7 @@ def main():
         o_cpu, lse_cpu = od.cpu(), lsed.cpu()
         cpu, parity = cpu_baseline(q, k, v, scale, causal, o_cpu, lse_cpu, args.cpu_budget)
 
+    traffic = read_traffic()
     line = {
         "metric": "attn fwd TFLOP/s & % bf16 MFMA peak (causal N=8192 d=128); softmax GB/s",
         "value": round(tflops, 2),
@@ -225,9 +310,13 @@ def main():
                     "ms_max": round(max(sm_ms), 4), "gbps": round(gbps, 1),
                     "bytes_per_launch": sm_bytes, "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic.get("attn_fwd_bf16"),
+                     "traffic_algorithmic_min": attn_min_bytes},
         "roofline_softmax": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
-                             "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+                             "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                             "traffic": traffic.get("softmax_rows"),
+                             "traffic_algorithmic": sm_bytes},
         "cpu_baseline": cpu,
         "parity": parity,
         "timing": {"method": "HIP events on the launch stream", "l2_flush": False,
