@@ -65,8 +65,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Word 3 of a raw (unformatted, byte-addressed) buffer resource on gfx9.
 constexpr int kBufferWord3 = 0x00020000;
 
-constexpr int kWaves = 4;
-constexpr int kBM = 32 * kWaves;  // query rows per block
+constexpr int kWaves = 8;                  // two groups of four, one of each per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGroupThreads = kThreads / 2;
+constexpr int kBM = 32 * kWaves;           // query rows per block
+constexpr int kRoundBytes = 16 * kGroupThreads;  // bytes one group-wide 16-byte copy moves
 constexpr int kBN = 64;           // keys per tile
 
 // Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
@@ -89,8 +92,8 @@ struct Layout {
     static constexpr int RB = 2 * D;            // bytes per row
     static constexpr int NCH = RB / 16;         // 16-byte chunks per row
     static constexpr int TILE = kBN * RB;       // bytes per tile
-    static constexpr int ROUNDS = TILE / 4096;  // 16-byte copies per thread per tile
-    static constexpr int ROWS_PER_ROUND = 4096 / RB;
+    static constexpr int ROUNDS = TILE / kRoundBytes;  // 16-byte copies per thread per tile
+    static constexpr int ROWS_PER_ROUND = kRoundBytes / RB;
     // K is read as 16-byte fragments by 32 lanes on 32 consecutive rows.
     __device__ static constexpr int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
     // V is read with the transposing 8-byte load on 8 consecutive rows x 4 chunks.
@@ -117,8 +120,9 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const lds_char*)(p));
 }
 
-// One tile of K or V from HBM straight to LDS.  Thread t writes LDS bytes
-// 4096 * round + 16 * t, i.e. row ROWS_PER_ROUND * round + t / NCH at chunk position
+// One tile of K or V from HBM straight to LDS, by one group of kGroupThreads threads.
+// Thread t of the group writes LDS bytes
+// kRoundBytes * round + 16 * t, i.e. row ROWS_PER_ROUND * round + t / NCH at chunk position
 // t % NCH, so it fetches logical chunk (t % NCH) ^ swz(row) of that row; `src_off` is
 // that per-thread byte offset within a round (the same for every round and tile,
 // because the swizzles repeat every ROWS_PER_ROUND rows).  The copy goes through a
@@ -135,7 +139,7 @@ __device__ __forceinline__ void tile_to_lds(char* lds_tile, const char* head, in
     char* dst = lds_tile + 1024 * (tid >> 6);  // wave-uniform; the lane offset is implicit
 #pragma unroll
     for (int r = 0; r < L::ROUNDS; ++r)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + 4096 * r), 16, src_off, 4096 * r,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + kRoundBytes * r), 16, src_off, kRoundBytes * r,
                                                  0, 0);
 }
 
@@ -148,8 +152,7 @@ struct Wave {
 
     bf16x8 qf[KS];   // Q^T fragments (B operand of S^T = K Q^T)
     f32x16 acc[DB];  // O^T accumulator: this lane's query row, 16 of each 32 outputs
-    bf16x8 pf[4];    // P^T fragments of the last finished tile (B operand of O^T += V^T P^T);
-                     // a tile's new fragments are formed while P V still reads the old ones
+    bf16x8 pf[4];    // P^T fragments of the last finished tile (B operand of O^T += V^T P^T)
     int k_off[KS];   // byte offset of this lane's K fragment for k-step ks (row l32)
     int v_off[DB];   // byte offset of this lane's transposing V block for output block b
     float m;         // reference max of |scale| log2(e) score, this lane's row (see kLazy)
@@ -157,7 +160,6 @@ struct Wave {
     float c;         // |scale| log2(e)
     float base;      // finite stand-in for m while a tile is exponentiated
     float alpha;     // exp2(m_old - m_new) of the tile in flight
-    float ps;        // partial row sum of the tile in flight
     int half, key_lim;
 
     // S^T = K Q^T for the two 32-key halves of a tile (A = K rows from LDS).
@@ -174,67 +176,56 @@ struct Wave {
         }
     }
 
-    // First half of the online-softmax update of a tile: hidden keys (diagonal /
-    // ragged tiles only) take no part; the row maximum moves the reference m if it
-    // exceeds it by more than kLazy; the first 32-key half is exponentiated and packed.
+    // Online-softmax update of one tile, in two parts.  prep (reads S only): the row
+    // maximum over the visible keys is taken and moves the reference m if it exceeds it
+    // by more than kLazy.  expsum: the 32 keys are exponentiated (hidden keys, on
+    // diagonal or ragged tiles only, get exactly 0), summed into l and packed to bf16
+    // P^T fragments.  Reductions run as four independent partial chains so that no
+    // instruction waits long on the one before it.
+    __device__ __forceinline__ bool visible(int j0, int sb, int r) const {
+        return j0 + 4 * half + 32 * sb + 8 * (r >> 2) + (r & 3) <= key_lim;
+    }
+
     template <bool MASK>
-    __device__ __forceinline__ void softmax_a(f32x16 (&st)[2], int j0) {
-        if (MASK) {
-            const int key0 = j0 + 4 * half;  // key of st[0][0]
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + 32 * sb + 8 * (r >> 2) + (r & 3);
-                    st[sb][r] = key <= key_lim ? st[sb][r] : kNegInf;
-                }
-        }
-        float mt = kNegInf;
+    __device__ __forceinline__ void prep(const f32x16 (&st)[2], int j0) {
+        float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, st[sb][r]);
-        mt = fmaxf(mt, swap_halves(mt)) * c;
+            for (int r = 0; r < 16; ++r)
+                mx[r & 3] = fmaxf(mx[r & 3], (!MASK || visible(j0, sb, r)) ? st[sb][r] : kNegInf);
+        const HalfPair pm = half_pair(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])));
+        const float mt = fmaxf(pm.lo, pm.hi) * c;
         // m = -inf (nothing seen yet) always moves: -inf + kLazy is -inf
         const float m_new = mt > m + kLazy ? mt : m;
         base = safe_base(m_new);
         alpha = fast_exp2(m - base);  // 1 when m stays; 0 when m = -inf
         m = m_new;
-        ps = 0.0f;
-        exp_half<MASK>(st[0], 0);
     }
 
-    // Second half: exponentiate and pack the other 32 keys, then update l.
     template <bool MASK>
-    __device__ __forceinline__ void softmax_b(f32x16 (&st)[2]) {
-        exp_half<MASK>(st[1], 1);
-        l = alpha * l + ps;
-    }
-
-    // Exponentiate 32 keys (half sb of the tile) and pack them to bf16 P^T fragments
-    // pf[2 sb], pf[2 sb + 1]; the row sum adds the packed pairs with v_dot2c_f32_bf16,
-    // so l sums exactly the weights that the P V product uses.
-    template <bool MASK>
-    __device__ __forceinline__ void exp_half(f32x16& x, int sb) {
+    __device__ __forceinline__ void expsum(f32x16 (&st)[2], int j0) {
+        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float e = fast_exp2(fmaf(x[r], c, -base));
-            // exactly 0 for hidden keys (exp2 of c * -inf is NaN when c = 0)
-            if (MASK) e = x[r] == kNegInf ? 0.0f : e;
-            x[r] = e;
-        }
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            u32x4 w;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const bf16x2 pr = __builtin_convertvector(f32x2{x[8 * hb + 2 * t], x[8 * hb + 2 * t + 1]}, bf16x2);
-                ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
-                w[t] = __builtin_bit_cast(uint32_t, pr);
+            for (int r = 0; r < 16; ++r) {
+                float e = fast_exp2(fmaf(st[sb][r], c, -base));
+                if (MASK) e = visible(j0, sb, r) ? e : 0.0f;
+                st[sb][r] = e;
+                sum[r & 3] += e;
             }
-            pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
-        }
+        l = alpha * l + ((sum[0] + sum[1]) + (sum[2] + sum[3]));
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                u32x4 w;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    w[t] = pack_bf16x2(st[sb][8 * hb + 2 * t], st[sb][8 * hb + 2 * t + 1]);
+                pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
+            }
     }
 
     // O^T *= alpha, skipped (per wavefront) when no row moved its reference maximum.
@@ -268,7 +259,7 @@ struct Wave {
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     using L = Layout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -292,6 +283,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
+    const int group = wave >> 2;  // waves w and w + 4 share a SIMD
+    const int gtid = tid & (kGroupThreads - 1);
     const int64_t head = (int64_t)bh * N * D;
     const char* kh = reinterpret_cast<const char*>(p.k + head);
     const char* vh = reinterpret_cast<const char*>(p.v + head);
@@ -301,7 +294,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     const bool wave_live = qw0 < N;
 
     // Per-thread source offsets of the HBM -> LDS copies (see tile_to_lds).
-    const int t_row = tid / L::NCH, t_pos = tid % L::NCH;
+    const int t_row = gtid / L::NCH, t_pos = gtid % L::NCH;
     const int k_src = t_row * L::RB + 16 * (t_pos ^ L::k_swz(t_row));
     const int v_src = t_row * L::RB + 16 * (t_pos ^ L::v_swz(t_row));
 
@@ -346,90 +339,101 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
     // tiles this wavefront needs (a prefix of the block's tiles)
     const int n_w = !wave_live ? 0 : CAUSAL ? min(n_kv, min(qw0 + 31, N - 1) / kBN + 1) : n_kv;
 
-    // Software pipeline over key tiles, three tiles deep.  Iteration j:
-    //   phase A: O += P_{j-1} V_{j-1} on the matrix cores, while the vector ALUs take
-    //            the row maximum of S_j and exponentiate its first half;
-    //   phase B: S_{j+1} = K_{j+1} Q^T on the matrix cores, while the vector ALUs
-    //            finish P_j and pack it to bf16;
-    //   then O *= alpha_j (rarely needed).  K_{j+2} and V_j travel from HBM to the LDS
-    //   buffers that iteration j-1 finished reading, during the iteration.
-    // K is two tiles ahead of V; one barrier per tile orders everything.
-    tile_to_lds<D>(k_lds0, kh, 0, N, tid, k_src);
-    if (n_kv > 1) tile_to_lds<D>(k_lds1, kh, kBN, N, tid, k_src);
+    // Ping-pong over key tiles.  For wave group g, the work on tile j is split into
+    //   GEMM_j    = O += P_{j-1} V_{j-1}, then S_{j+1} = K_{j+1} Q^T  (matrix cores)
+    //   SOFTMAX_j = P_j and alpha_j from S_j, then O *= alpha_j       (vector ALUs)
+    // and group g runs GEMM_j in half-step 2 j + g and SOFTMAX_j in half-step 2 j + 1 + g.
+    // The two wavefronts that share a SIMD are in different groups, so one always has
+    // matrix work while the other has vector work.  At half-step 2 j, K_{j+2} (copied
+    // by group 0 during its GEMM) and V_j (copied by group 1 during its SOFTMAX) go
+    // from HBM to the LDS buffers that GEMM_{j-1} finished reading; each has until the
+    // barrier after half-step 2 j + 1 to land.
+    if (group == 0 || n_kv > 1) tile_to_lds<D>(group ? k_lds1 : k_lds0, kh, group ? kBN : 0, N, gtid, k_src);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies have landed
     __syncthreads();
     f32x16 sa[2], sb[2];
     if (n_w > 0) w.qk(sa, k_lds0);
     __syncthreads();  // K buffer 0 may now be refilled
 
-    // PAR = j % 2 at compile time, so every buffer access names one LDS object.
-    auto step = [&](auto par, int j, f32x16(&sc)[2], f32x16(&sn)[2]) {
+    auto is_masked = [&](int j) { return (CAUSAL && j * kBN + kBN - 1 > qw0) || (j * kBN + kBN > N); };
+    // GEMM_j (plus, for group 0, the copy of K_{j+2}).  PAR = j % 2 at compile time,
+    // so every buffer access names one LDS object.
+    auto gemm = [&](auto par, int j, f32x16(&sn)[2], bool copy_k) {
         constexpr int PAR = decltype(par)::value;
-        char* k_fill = PAR ? k_lds1 : k_lds0;       // gets K_{j+2}
-        char* v_fill = PAR ? v_lds1 : v_lds0;       // gets V_j
-        const char* knext = PAR ? k_lds0 : k_lds1;  // holds K_{j+1}
         const char* vprev = PAR ? v_lds0 : v_lds1;  // holds V_{j-1}
-        const int j0 = j * kBN;
-        const bool do_pv = j >= 1 && j - 1 < n_w;  // O += P_{j-1} V_{j-1}
-        const bool do_sm = j < n_w;                // softmax of tile j
-        const bool do_qk = j + 1 < n_w;            // S_{j+1}
-        if (j + 2 < n_kv) tile_to_lds<D>(k_fill, kh, j0 + 2 * kBN, N, tid, k_src);
-        tile_to_lds<D>(v_fill, vh, j0, N, tid, v_src);
-        const bool mask = (CAUSAL && j0 + kBN - 1 > qw0) || (j0 + kBN > N);
-        if (do_pv && do_sm && do_qk && !mask) {
+        const char* knext = PAR ? k_lds0 : k_lds1;  // holds K_{j+1}
+        const bool do_pv = j >= 1 && j - 1 < n_w;
+        const bool do_qk = j + 1 < n_w;
+        __builtin_amdgcn_s_setprio(1);
+        if (do_pv && do_qk) {
+            if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gtid, k_src);
             w.pv(vprev);
-            w.template softmax_a<false>(sc, j0);
-            // Phase A: each matrix instruction (32 cycles) is paired with two
-            // transposing V reads for a later one and a run of vector instructions.
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-            }
             w.qk(sn, knext);
-            w.template softmax_b<false>(sc);
-            // Phase B: each matrix instruction paired with one K read for a later one.
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            // Keep LDS operand reads a few matrix instructions ahead of their use and
+            // spread the copies between the matrix instructions.
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i < 14) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < 10) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         } else {
+            if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gtid, k_src);
             if (do_pv) w.pv(vprev);
-            if (do_sm) {
-                if (mask)
-                    w.template softmax_a<true>(sc, j0);
-                else
-                    w.template softmax_a<false>(sc, j0);
-            }
             if (do_qk) w.qk(sn, knext);
-            if (do_sm) {
-                if (mask)
-                    w.template softmax_b<true>(sc);
-                else
-                    w.template softmax_b<false>(sc);
-            }
         }
-        if (do_sm) w.rescale();  // O (now holding tile j-1) *= alpha_j before P_j V_j
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this iteration's copies have landed
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto softmax = [&](int j, f32x16(&sc)[2]) {
+        if (j < 0 || j >= n_w) return;
+        if (is_masked(j)) {
+            w.template prep<true>(sc, j * kBN);
+            w.template expsum<true>(sc, j * kBN);
+        } else {
+            w.template prep<false>(sc, j * kBN);
+            w.template expsum<false>(sc, j * kBN);
+        }
+        w.rescale();  // O (holding tiles up to j-1) *= alpha_j before P_j V_j
+    };
+    // One tile step: S_j is in s_cur, S_{j-1} (or nothing) in s_oth, which GEMM_j
+    // refills with S_{j+1}.
+    auto step = [&](auto par, int j, f32x16(&s_cur)[2], f32x16(&s_oth)[2]) {
+        constexpr int PAR = decltype(par)::value;
+        // half-step 2 j
+        if (group == 0) {
+            gemm(par, j, s_oth, j + 2 < n_kv);
+        } else {
+            if (j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gtid, v_src);
+            softmax(j - 1, s_oth);
+        }
+        __syncthreads();
+        // half-step 2 j + 1
+        if (group == 0) {
+            softmax(j, s_cur);
+        } else {
+            gemm(par, j, s_oth, false);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K_{j+2} and V_j have landed
         __syncthreads();
     };
 
     int j = 0;
-    for (; j + 1 < n_kv; j += 2) {
+    for (; j + 1 <= n_kv; j += 2) {
         step(std::integral_constant<int, 0>{}, j, sa, sb);
         step(std::integral_constant<int, 1>{}, j + 1, sb, sa);
     }
-    if (j < n_kv) step(std::integral_constant<int, 0>{}, j, sa, sb);
-    // the last tile's P V (its V went to buffer (n_kv - 1) % 2)
-    if (n_w == n_kv && n_w > 0) w.pv(((n_kv - 1) & 1) ? v_lds1 : v_lds0);
+    if (j <= n_kv) step(std::integral_constant<int, 0>{}, j, sa, sb);
 
     if (!wave_live) return;
-    const float l_row = w.l + swap_halves(w.l);
+    const HalfPair pl = half_pair(w.l);
+    const float l_row = pl.lo + pl.hi;
     if (my_q < N) {
         const float inv = 1.0f / l_row;
         uint16_t* orow = p.o + head + (int64_t)my_q * D;
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(Params p) {
 
 template <int D, bool CAUSAL>
 hipError_t launch(const Params& p, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 

@@ -67,4 +67,16 @@ __device__ __forceinline__ MLState merge_group(MLState s) {
 // `x` from lane l ^ 32.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
+// The values of `x` in lanes l mod 32 and l mod 32 + 32, delivered to every lane l by
+// one v_permlane32_swap (a vector-ALU exchange, no LDS round trip).  Reductions over
+// the pair, such as lo + hi, come out bitwise identical in both lanes.
+struct HalfPair {
+    float lo, hi;
+};
+__device__ __forceinline__ HalfPair half_pair(float x) {
+    const unsigned u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return HalfPair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 }  // namespace mi355
