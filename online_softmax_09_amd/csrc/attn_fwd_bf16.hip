@@ -130,13 +130,14 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
 // arithmetic is scalar, and rows at or past N (last tile only) read as zeros, whose
 // scores are masked and whose probabilities are 0.
 template <int D>
-__device__ __forceinline__ void tile_to_lds(char* lds_tile, const char* head, int j0, int N, int tid,
+__device__ __forceinline__ void tile_to_lds(char* lds_tile, const char* head, int j0, int N, int gwave,
                                             int src_off) {
     using L = Layout<D>;
     const int rows = min(N - j0, kBN);
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(head + (int64_t)j0 * L::RB), (short)0, rows * L::RB, kBufferWord3);
-    char* dst = lds_tile + 1024 * (tid >> 6);  // wave-uniform; the lane offset is implicit
+    char* dst = lds_tile + 1024 * gwave;  // gwave: the wave's index in its group (uniform);
+                                          // the lane offset is implicit
 #pragma unroll
     for (int r = 0; r < L::ROUNDS; ++r)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + kRoundBytes * r), 16, src_off, kRoundBytes * r,
@@ -285,6 +286,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     const int lane = tid & 63;
     const int group = wave >> 2;  // waves w and w + 4 share a SIMD
     const int gtid = tid & (kGroupThreads - 1);
+    // The wavefront's index in its group, read from lane 0 so the compiler knows it is
+    // uniform: the LDS copy destinations are then scalar.
+    const int gwave = __builtin_amdgcn_readfirstlane(wave & 3);
     const int64_t head = (int64_t)bh * N * D;
     const char* kh = reinterpret_cast<const char*>(p.k + head);
     const char* vh = reinterpret_cast<const char*>(p.v + head);
@@ -348,7 +352,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     // by group 0 during its GEMM) and V_j (copied by group 1 during its SOFTMAX) go
     // from HBM to the LDS buffers that GEMM_{j-1} finished reading; each has until the
     // barrier after half-step 2 j + 1 to land.
-    if (group == 0 || n_kv > 1) tile_to_lds<D>(group ? k_lds1 : k_lds0, kh, group ? kBN : 0, N, gtid, k_src);
+    {
+        const int ug = __builtin_amdgcn_readfirstlane(group);  // uniform copy of the group
+        if (ug == 0 || n_kv > 1) tile_to_lds<D>(ug ? k_lds1 : k_lds0, kh, ug ? kBN : 0, N, gwave, k_src);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies have landed
     __syncthreads();
     f32x16 sa[2], sb[2];
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
         const bool do_qk = j + 1 < n_w;
         __builtin_amdgcn_s_setprio(1);
         if (do_pv && do_qk) {
-            if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gtid, k_src);
+            if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gwave, k_src);
             w.pv(vprev);
             w.qk(sn, knext);
             // Keep LDS operand reads a few matrix instructions ahead of their use and
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
                 if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         } else {
-            if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gtid, k_src);
+            if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gwave, k_src);
             if (do_pv) w.pv(vprev);
             if (do_qk) w.qk(sn, knext);
         }
@@ -410,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
         if (group == 0) {
             gemm(par, j, s_oth, j + 2 < n_kv);
         } else {
-            if (j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gtid, v_src);
+            if (j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
             softmax(j - 1, s_oth);
         }
         __syncthreads();
