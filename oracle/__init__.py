@@ -15,6 +15,8 @@ fp32 / bf16 inputs, by the plain definition of the operation:
   semantics the GPU tree reduction must reproduce.
 * ``attention`` — standard attention with the score matrix S materialised,
   softmax by the same three passes, ``O = P V`` and ``LSE = m + ln l``.
+* ``attention_bwd`` — the gradients dQ, dK, dV of that definition for an upstream dO,
+  by the chain rule with S, P, dP and dS materialised.
 
 Pages cited (titles as they appear on the pages; section numbers are the pages'):
 
@@ -43,3 +45,4 @@ from .softmax import (  # noqa: F401
     weighted_full,
 )
 from .attention import attention, attention_rows  # noqa: F401
+from .attention_bwd import attention_backward  # noqa: F401
