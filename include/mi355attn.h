@@ -17,6 +17,9 @@
  *   where the (m, l) state of a row is reduced as a tree with the merge rule
  *   m = max(m_a, m_b), l = l_a exp(m_a - m) + l_b exp(m_b - m).
  *
+ *   Attention gradients (fa_bwd), same page, section 7.2: dQ, dK, dV of the forward,
+ *   recomputing the probabilities tile by tile from the saved per-row LSE.
+ *
  * Conventions shared by every entry point:
  *
  *   Memory     All pointers are device pointers to memory owned by the caller.  The
@@ -98,6 +101,35 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  * otherwise; it is written once.  Inputs must be finite.
  */
 int online_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream);
+
+/*
+ * fa_bwd — gradients of the bf16 attention of fa_fwd, recomputing the probabilities.
+ *
+ * Operation: "Softmax numerical stability and IO-aware attention" (zhouzhq2021.github.io),
+ * section 7.2 and question 4: the backward pass keeps only per-row statistics from the
+ * forward and recomputes the local scores tile by tile instead of storing the N x N
+ * probability matrix.  The gradients are the derivative of O = softmax(scale Q K^T) V:
+ *   P = exp(scale Q K^T - LSE),  dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *   D_i = dO_i . O_i,  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ *   q, k, v    [B, H, N, d] bf16, the forward's inputs, read only.
+ *   o, lse     the forward's outputs for the same q, k, v, scale and causal (fa_fwd), read only.
+ *   dout       [B, H, N, d] bf16, the upstream gradient dL/dO, read only.
+ *   dq, dk, dv [B, H, N, d] bf16, written (float32 accumulation, rounded once).
+ *   workspace  device memory of fa_bwd_workspace_bytes(B, H, N) bytes, 16-byte aligned, owned by
+ *              the caller; overwritten (per-row D and LSE log2(e), float32).  It may be reused
+ *              as soon as the stream has run this call.
+ *   B, H, N, d, scale, causal, stream  as for fa_fwd.
+ *
+ * dq, dk, dv and workspace must not overlap each other or any input.  Each gradient element
+ * is produced by one thread (no atomics), so results are bitwise repeatable.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Bytes of workspace fa_bwd needs for B x H heads of N rows (8 per row); -1 if B, H or N < 1. */
+int64_t fa_bwd_workspace_bytes(int B, int H, int N);
 
 /* Human-readable name of a return code (static string, never NULL). */
 const char* mi355attn_strerror(int code);

@@ -11,13 +11,15 @@ Functions carry the names of the C entry points:
 * ``fa_fwd(q, k, v, scale, causal)``      bf16 [B, H, N, d] -> (o bf16, lse float32 [B, H, N])
 * ``fa_fwd_f32(q, k, v, scale, causal)``  the same in float32
 * ``online_softmax_rows(x)``              float32 [rows, cols] -> softmax of every row
+* ``fa_bwd(q, k, v, o, lse, dout, scale, causal)``  bf16 -> (dq, dk, dv), the gradients
+  of ``fa_fwd`` for the upstream gradient ``dout``
 """
 
 import math
 
 from . import _lib
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "online_softmax_rows", "library_path", "version"]
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "online_softmax_rows", "library_path", "version"]
 
 
 def library_path():
@@ -93,6 +95,41 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
 def fa_fwd_f32(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """float32 attention forward on the GPU; returns (o, lse).  scale defaults to 1/sqrt(d)."""
     return _attention("fa_fwd_f32", q, k, v, scale, causal, out, lse, stream, _torch().float32)
+
+
+def fa_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
+           stream=None):
+    """Gradients (dq, dk, dv) of the bf16 attention forward for the upstream gradient dout.
+
+    o and lse are fa_fwd's outputs for the same q, k, v, scale and causal.  The float32
+    workspace the library needs (8 bytes per row) is allocated here unless given.
+    """
+    torch = _torch()
+    _attention_args(q, k, v, torch.bfloat16, o, lse)
+    _attention_args(q, k, dout, torch.bfloat16, None, lse)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    grads = []
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if g is None:
+            g = torch.empty_like(q)
+        if g.shape != q.shape or g.dtype != torch.bfloat16 or not g.is_contiguous() or g.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bf16 tensor like q")
+        grads.append(g)
+    lib = _lib.load()
+    need = lib.fa_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    if (workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.device != q.device
+            or workspace.numel() * 4 < need):
+        raise ValueError(f"workspace must be a contiguous float32 tensor of at least {need} bytes on q's device")
+    with torch.cuda.device(q.device):
+        rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                        grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), workspace.data_ptr(),
+                        B, H, N, d, float(scale), 1 if causal else 0, _stream_handle(stream, q.device))
+    _lib.check(rc, "fa_bwd")
+    return tuple(grads)
 
 
 def online_softmax_rows(x, out=None, stream=None):

@@ -22,6 +22,8 @@ SIGNATURES = {
     "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
     "fa_fwd_f32": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
     "online_softmax_rows": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp]),
+    "fa_bwd": (_c_int, [_vp] * 10 + [_c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
+    "fa_bwd_workspace_bytes": (_c_i64, [_c_int, _c_int, _c_int]),
     "mi355attn_strerror": (ctypes.c_char_p, [_c_int]),
     "mi355attn_last_hip_error": (_c_int, []),
     "mi355attn_version": (_c_int, []),

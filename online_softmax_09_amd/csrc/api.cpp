@@ -74,6 +74,39 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                                              static_cast<hipStream_t>(stream)));
 }
 
+int64_t fa_bwd_workspace_bytes(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1) return -1;
+    return (int64_t)B * H * N * 2 * (int64_t)sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, void* workspace, int B, int H, int N, int d, float scale, int causal,
+           void* stream) {
+    // q, k, v, o and lse as for the forward (o is only read here)
+    const int rc = check_attention(q, k, v, o, lse, B, H, N, d, scale, 2);
+    if (rc != MI355ATTN_OK) return rc;
+    if (causal != 0 && causal != 1) return MI355ATTN_ERR_INVALID_ARG;
+    if (!dout || !dq || !dk || !dv || !workspace) return MI355ATTN_ERR_INVALID_ARG;
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+        return MI355ATTN_ERR_INVALID_ARG;
+    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+    const uint64_t tb = rows * (uint64_t)d * 2;
+    const uint64_t lb = rows * sizeof(float);
+    const uint64_t wb = 2 * lb;
+    const void* outs[4] = {dq, dk, dv, workspace};
+    const uint64_t out_bytes[4] = {tb, tb, tb, wb};
+    const void* ins[6] = {q, k, v, o, dout, lse};
+    const uint64_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return MI355ATTN_ERR_INVALID_ARG;
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return MI355ATTN_ERR_INVALID_ARG;
+    }
+    return finish(mi355::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), B,
+                                              H, N, d, scale, causal != 0, static_cast<hipStream_t>(stream)));
+}
+
 int online_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream) {
     if (rows < 0 || cols < 1) return MI355ATTN_ERR_INVALID_ARG;
     if (rows == 0) return MI355ATTN_OK;

@@ -1,0 +1,465 @@
+// attn_bwd_bf16.hip — gradients of bf16 attention (dQ, dK, dV) on gfx950 matrix cores,
+// recomputing the probabilities from the row statistics saved by the forward.
+//
+// What is computed: for O = softmax(scale Q K^T) V (causal or not) and an upstream
+// gradient dO, the derivative of that definition,
+//     P = exp(scale Q K^T - LSE)        (recomputed; LSE = m + ln l from the forward)
+//     dV = P^T dO,   dP = dO V^T,   dS = P * (dP - D),   D_i = dO_i . O_i
+//     dQ = scale dS K,   dK = scale dS^T Q.
+// D_i equals sum_j P_ij dP_ij (the softmax Jacobian's row term) because O_i = sum_j
+// P_ij V_j.  Keeping only LSE and recomputing P tile by tile instead of storing the
+// N x N probabilities is the pages' account of the backward pass ("Softmax numerical
+// stability and IO-aware attention", section 7.2 and question 4).
+//
+// Three kernels, enqueued in order on one stream:
+//   1. prep: D_i = dO_i . O_i and LSE_i log2(e) per row, into the caller's workspace.
+//   2. dQ: one block per 128 query rows, 4 wavefronts of 32 rows, streaming 64-key
+//      tiles of K and V through LDS.  The layout is the forward's: S^T = K Q^T and
+//      dP^T = V dO^T put one query row in each lane (Q and dO fragments stay in
+//      registers), dS^T is formed in place and packed to bf16, and
+//      dQ^T += K^T dS^T reads K^T with the transposing LDS load.
+//   3. dK/dV: one block per 128 keys, 4 wavefronts of 32 keys, streaming 64-row tiles
+//      of Q, dO, LSE and D through LDS.  Here S = Q K^T and dP = dO V^T put one key in
+//      each lane (K and V fragments stay in registers); P and dS, packed to bf16 as
+//      they lie, are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
+//      operands are transposing reads of the dO and Q tiles.
+// Computing dQ in its own pass (recomputing S and dP there) keeps every gradient
+// element owned by one lane of one block: no atomics, and results are bitwise
+// repeatable.
+//
+// LDS tiles are unpadded rows with 16-byte chunks XOR-permuted by swz(row), a
+// permutation under which both access patterns used on the same tile are free of
+// bank conflicts: 16-byte reads of one chunk of 16 consecutive rows, and transposing
+// reads of 32 bytes from rows 4h..4h+3 of an 8-row group.
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "launchers.hpp"
+#include "mfma_bf16.hpp"
+
+namespace mi355 {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdRows = 32 * kBwdWaves;    // query rows (dQ) or keys (dK/dV) per block
+constexpr int kT = 64;                      // rows per streamed tile
+constexpr int kBwdRound = 16 * kBwdThreads; // bytes one block-wide 16-byte copy moves
+
+template <int D>
+struct BLayout {
+    static constexpr int RB = 2 * D;               // bytes per row
+    static constexpr int NCH = RB / 16;            // 16-byte chunks per row
+    static constexpr int TILE = kT * RB;           // bytes per tile
+    static constexpr int ROUNDS = TILE / kBwdRound;
+    // Chunk position of logical chunk c in row r is c ^ swz(r).  d = 128 (a row spans
+    // all 64 banks): the low two bits of the row pick bits 2..3 of the permutation and
+    // bits 2..3 of the row pick bits 0..1, so 16 consecutive rows see 16 different
+    // positions and rows 4h..4h+3 see chunk pairs {c, c+1} at 4 different places.
+    // d = 64 (two rows per bank line): the same with row bit 1 in place of bits 0..1.
+    // Both depend only on row mod 16, which the per-round copy offsets rely on.
+    __device__ static constexpr int swz(int r) {
+        return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    }
+};
+
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* dout;
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    const float* delta;  // [B*H*N]  D_i = dO_i . O_i
+    const float* lse2;   // [B*H*N]  LSE_i * log2(e)
+    int N;
+    int n_tiles;         // ceil(N / kBwdRows)
+    int n_blocks;
+    float c;             // scale * log2(e)
+    float scale;
+};
+
+// One 64-row tile of a [N, D] bf16 slab (rows r0 .. r0 + 63 of `head`) from HBM
+// straight to LDS, by all kBwdThreads threads of the block; `src_off` is the thread's
+// fixed source offset within a round (see the kernels).  Rows at or past N read as
+// zeros; live = false fills the tile with zeros without reading memory.
+template <int D>
+__device__ __forceinline__ void tile_to_lds(char* lds, const uint16_t* head, int r0, int N, int wave,
+                                            int src_off, bool live) {
+    using L = BLayout<D>;
+    const int rows = live ? min(N - r0, kT) : 0;
+    const char* base = reinterpret_cast<const char*>(head) + (live ? (int64_t)r0 * L::RB : 0);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows * L::RB, kBufferWord3);
+    char* dst = lds + 1024 * wave;  // the wave's 1 KiB of each round; lane offset implicit
+#pragma unroll
+    for (int r = 0; r < L::ROUNDS; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + kBwdRound * r), 16, src_off,
+                                                 kBwdRound * r, 0, 0);
+}
+
+// 64 floats (rows r0 .. r0 + 63 of a per-row vector) to LDS by one wavefront; rows at
+// or past N read as zeros.
+__device__ __forceinline__ void rowvec_to_lds(float* lds, const float* vec, int r0, int N, int lane, bool live) {
+    const int rows = live ? min(N - r0, kT) : 0;
+    const float* base = vec + (live ? r0 : 0);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows * 4, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, 4 * lane, 0, 0, 0);
+}
+
+// Per-lane LDS offsets for the two access patterns on a BLayout<D> tile.
+template <int D>
+struct TileReads {
+    using L = BLayout<D>;
+    static constexpr int KS = D / 16;
+    static constexpr int DB = D / 32;
+    int row[KS];    // 16-byte read of row l32 (+32 sb), logical chunk 2 ks + h
+    int tr_lo[DB];  // transposing read for output columns 32 b .. 32 b + 31, rows 4h + (lane%16)/4
+    int tr_hi[DB];  // the same 8 rows further down
+    __device__ void init(int lane) {
+        const int l32 = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) row[ks] = l32 * L::RB + 16 * ((2 * ks + h) ^ L::swz(l32));
+        const int vr = 4 * h + ((lane & 15) >> 2);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const int col = 64 * b + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+            tr_lo[b] = vr * L::RB + 16 * ((col >> 4) ^ L::swz(vr)) + (col & 15);
+            tr_hi[b] = (vr + 8) * L::RB + 16 * ((col >> 4) ^ L::swz(vr + 8)) + (col & 15);
+        }
+    }
+};
+
+// acc (32 rows of the tile from row 32 sb, x 32 columns) = A B: A = 16-byte row reads of
+// `tile` (rows = the accumulator's rows, k = the D columns), B = frag (per lane: column
+// l32, k-slots 8h..8h+7 of each 16-wide k-step).
+template <int D>
+__device__ __forceinline__ f32x16 rows_times_frag(const char* tile, int sb, const TileReads<D>& rd,
+                                                  const bf16x8 (&frag)[D / 16]) {
+    f32x16 a = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 t = *reinterpret_cast<const bf16x8*>(tile + 32 * sb * BLayout<D>::RB + rd.row[ks]);
+        a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t, frag[ks], a, 0, 0, 0);
+    }
+    return a;
+}
+
+// acc[b] (output columns 32 b.., x 32 lanes' columns) += T^T B over the 16 tile rows
+// of group g: A = transposing reads of `tile`, B = the packed operand for group g.
+template <int D>
+__device__ __forceinline__ void trans_times_packed(f32x16 (&acc)[D / 32], const char* tile, int g,
+                                                   const TileReads<D>& rd, const bf16x8& bop) {
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b) {
+        const char* base = tile + 16 * g * BLayout<D>::RB;
+        const bf16x8 a = lds_read_tr_pair(base + rd.tr_lo[b], base + rd.tr_hi[b]);
+        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[b], 0, 0, 0);
+    }
+}
+
+// Fragment of a row-major [*, D] bf16 slab for a B operand: lane supplies row `row`,
+// columns 16 ks + 8 h .. + 7.
+template <int D>
+__device__ __forceinline__ void load_frag(bf16x8 (&f)[D / 16], const uint16_t* slab, int row, int h) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        f[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(slab + (int64_t)row * D + 16 * ks + 8 * h));
+}
+
+// Packs 8 consecutive accumulator entries (v = 8 t .. 8 t + 7) into one bf16x8 B operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int t) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[8 * t + 2 * i], x[8 * t + 2 * i + 1]);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// Stores an accumulator pair layout (lane: row `row` of the output, columns
+// 32 b + 8 (v/4) + 4 h + v%4) as bf16, multiplied by `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* out, int row, int h, const f32x16 (&acc)[D / 32], float mul) {
+    uint16_t* orow = out + (int64_t)row * D;
+#pragma unroll
+    for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u32x2 o2;
+            o2[0] = pack_bf16x2(acc[b][4 * i + 0] * mul, acc[b][4 * i + 1] * mul);
+            o2[1] = pack_bf16x2(acc[b][4 * i + 2] * mul, acc[b][4 * i + 3] * mul);
+            *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * i + 4 * h) = o2;
+        }
+}
+
+// Logical block id -> (head, tile) with the forward's XCD-aware remap; causal grids
+// run their longest tiles first (`longest_last`: the tile index with the most work is
+// the last one for dQ, the first one for dK/dV).
+__device__ __forceinline__ void block_coords(const BwdParams& p, bool causal, bool longest_last, int& bh, int& t) {
+    const int nb = p.n_blocks;
+    int lid = blockIdx.x;
+    if ((nb & 7) == 0) lid = (lid & 7) * (nb >> 3) + (lid >> 3);
+    bh = lid / p.n_tiles;
+    t = lid % p.n_tiles;
+    if (causal && longest_last) t = p.n_tiles - 1 - t;
+}
+
+// ---------------------------------------------------------------------------------
+// 1. D_i = dO_i . O_i and LSE_i log2(e), one row per D/8 lanes.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const uint16_t* o, const uint16_t* dout, const float* lse,
+                                                            float* delta, float* lse2, int64_t rows) {
+    constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / LPR;
+    const int part = (int)(gid % LPR);
+    float acc = 0.0f;
+    if (row < rows) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * part);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * part);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+            acc = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (row < rows && part == 0) {
+        delta[row] = acc;
+        lse2[row] = lse[row] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// 2. dQ.  Lane: query row q = q0 + 32 wave + l32; S^T / dP^T rows are keys.
+// ---------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
+    using L = BLayout<D>;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    __shared__ __attribute__((aligned(1024))) char k_lds[2][L::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds[2][L::TILE];
+
+    int bh, qt;
+    block_coords(p, CAUSAL, true, bh, qt);
+    const int N = p.N;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t head = (int64_t)bh * N * D;
+    const int q0 = qt * kBwdRows;
+    const int qw0 = q0 + 32 * wave;
+    const int my_q = qw0 + l32;
+    const int q_row = min(my_q, N - 1);  // rows past the end compute garbage, never stored
+
+    const int t_row = tid / L::NCH, t_pos = tid % L::NCH;
+    const int src_off = t_row * L::RB + 16 * (t_pos ^ L::swz(t_row));
+    TileReads<D> rd;
+    rd.init(lane);
+
+    bf16x8 qf[KS], dof[KS];
+    load_frag<D>(qf, p.q + head, q_row, h);
+    load_frag<D>(dof, p.dout + head, q_row, h);
+    const float lse2 = p.lse2[(int64_t)bh * N + q_row];
+    const float dlt = p.delta[(int64_t)bh * N + q_row];
+    const int key_lim = CAUSAL ? min(N - 1, my_q) : N - 1;
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+
+    const int q_last = min(q0 + kBwdRows - 1, N - 1);
+    const int n_kv = CAUSAL ? q_last / kT + 1 : (N + kT - 1) / kT;
+    const bool wave_live = qw0 < N;
+    const int n_w = !wave_live ? 0 : CAUSAL ? min(n_kv, min(qw0 + 31, N - 1) / kT + 1) : n_kv;
+
+    tile_to_lds<D>(k_lds[0], p.k + head, 0, N, wave, src_off, true);
+    tile_to_lds<D>(v_lds[0], p.v + head, 0, N, wave, src_off, true);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    for (int j = 0; j < n_kv; ++j) {
+        const int cur = j & 1;
+        // prefetch the next tile into the other buffers (read two barriers ago)
+        tile_to_lds<D>(k_lds[cur ^ 1], p.k + head, (j + 1) * kT, N, wave, src_off, j + 1 < n_kv);
+        tile_to_lds<D>(v_lds[cur ^ 1], p.v + head, (j + 1) * kT, N, wave, src_off, j + 1 < n_kv);
+        if (j < n_w) {
+            const char* kt = k_lds[cur];
+            const char* vt = v_lds[cur];
+            const int j0 = j * kT;
+            const bool masked = (CAUSAL && j0 + kT - 1 > qw0) || (j0 + kT > N);
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                f32x16 s = rows_times_frag<D>(kt, sb, rd, qf);    // S^T rows = keys
+                f32x16 dp = rows_times_frag<D>(vt, sb, rd, dof);  // dP^T
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float pr = fast_exp2(fmaf(s[r], p.c, -lse2));
+                    if (masked) {
+                        const int key = j0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        pr = key <= key_lim ? pr : 0.0f;
+                    }
+                    s[r] = pr * (dp[r] - dlt);  // dS^T
+                }
+                trans_times_packed<D>(acc, kt, 2 * sb + 0, rd, pack8(s, 0));
+                trans_times_packed<D>(acc, kt, 2 * sb + 1, rd, pack8(s, 1));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tiles have landed
+        __syncthreads();
+    }
+    if (wave_live && my_q < N) store_rows<D>(p.dq + head, my_q, h, acc, p.scale);
+}
+
+// ---------------------------------------------------------------------------------
+// 3. dK and dV.  Lane: key kc = k0 + 32 wave + l32; S / dP rows are queries.
+// ---------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+    using L = BLayout<D>;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    __shared__ __attribute__((aligned(1024))) char q_lds[2][L::TILE];
+    __shared__ __attribute__((aligned(1024))) char do_lds[2][L::TILE];
+    __shared__ __attribute__((aligned(16))) float lse_lds[2][kT];
+    __shared__ __attribute__((aligned(16))) float dl_lds[2][kT];
+
+    int bh, kt;
+    block_coords(p, CAUSAL, false, bh, kt);
+    const int N = p.N;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t head = (int64_t)bh * N * D;
+    const int64_t rowbase = (int64_t)bh * N;
+    const int k0 = kt * kBwdRows;
+    const int kw0 = k0 + 32 * wave;
+    const int my_k = kw0 + l32;
+    const int k_row = min(my_k, N - 1);
+
+    const int t_row = tid / L::NCH, t_pos = tid % L::NCH;
+    const int src_off = t_row * L::RB + 16 * (t_pos ^ L::swz(t_row));
+    TileReads<D> rd;
+    rd.init(lane);
+
+    bf16x8 kf[KS], vf[KS];
+    load_frag<D>(kf, p.k + head, k_row, h);
+    load_frag<D>(vf, p.v + head, k_row, h);
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int b = 0; b < DB; ++b) dk[b] = dv[b] = f32x16{};
+
+    // query tiles: causal blocks start at the tile holding their first key
+    const int i_begin = CAUSAL ? k0 / kT : 0;
+    const int n_q = (N + kT - 1) / kT;
+    const bool wave_live = kw0 < N;
+
+    auto copy_tile = [&](int buf, int i, bool live) {
+        tile_to_lds<D>(q_lds[buf], p.q + head, i * kT, N, wave, src_off, live);
+        tile_to_lds<D>(do_lds[buf], p.dout + head, i * kT, N, wave, src_off, live);
+        if (wave == 0) rowvec_to_lds(lse_lds[buf], p.lse2 + rowbase, i * kT, N, lane, live);
+        if (wave == 1) rowvec_to_lds(dl_lds[buf], p.delta + rowbase, i * kT, N, lane, live);
+    };
+    copy_tile(0, i_begin, i_begin < n_q);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    for (int i = i_begin; i < n_q; ++i) {
+        const int cur = (i - i_begin) & 1;
+        copy_tile(cur ^ 1, i + 1, i + 1 < n_q);
+        const char* qt = q_lds[cur];
+        const char* dt = do_lds[cur];
+        const int i0 = i * kT;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int qs0 = i0 + 32 * sb;  // first query of the sub-block
+            // causal: skip sub-blocks whose queries all precede this wave's keys
+            if (!wave_live || (CAUSAL && qs0 + 31 < kw0) || qs0 >= N) continue;
+            const bool masked = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
+            f32x16 s = rows_times_frag<D>(qt, sb, rd, kf);    // S rows = queries
+            f32x16 dp = rows_times_frag<D>(dt, sb, rd, vf);   // dP
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE and D vectors
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_lds[cur][32 * sb + 8 * g + 4 * h]);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_lds[cur][32 * sb + 8 * g + 4 * h]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * g + u;
+                    float pr = fast_exp2(fmaf(s[r], p.c, -l4[u]));
+                    if (masked) {
+                        const int qq = qs0 + 8 * g + 4 * h + u;
+                        pr = (qq < N && (!CAUSAL || qq >= my_k)) ? pr : 0.0f;
+                    }
+                    s[r] = pr;
+                    dp[r] = pr * (dp[r] - d4[u]);  // dS
+                }
+            }
+            trans_times_packed<D>(dv, dt, 2 * sb + 0, rd, pack8(s, 0));
+            trans_times_packed<D>(dv, dt, 2 * sb + 1, rd, pack8(s, 1));
+            trans_times_packed<D>(dk, qt, 2 * sb + 0, rd, pack8(dp, 0));
+            trans_times_packed<D>(dk, qt, 2 * sb + 1, rd, pack8(dp, 1));
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    }
+    if (wave_live && my_k < N) {
+        store_rows<D>(p.dv + head, my_k, h, dv, 1.0f);
+        store_rows<D>(p.dk + head, my_k, h, dk, p.scale);
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_main(BwdParams p, hipStream_t st) {
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kBwdThreads), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kBwdThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,
+                                int N, int d, float scale, bool causal, hipStream_t st) {
+    const int64_t rows = (int64_t)B * H * N;
+    BwdParams p;
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.dq = static_cast<uint16_t*>(dq);
+    p.dk = static_cast<uint16_t*>(dk);
+    p.dv = static_cast<uint16_t*>(dv);
+    p.delta = workspace;
+    p.lse2 = workspace + rows;
+    p.N = N;
+    p.n_tiles = (N + kBwdRows - 1) / kBwdRows;
+    const int64_t blocks = (int64_t)B * H * p.n_tiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    p.n_blocks = (int)blocks;
+    p.c = scale * kLog2e;
+    p.scale = scale;
+
+    const int lpr = d / 8;
+    const int64_t prep_blocks = (rows * lpr + 255) / 256;
+    if (prep_blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (d == 64)
+        hipLaunchKernelGGL((attn_bwd_prep_kernel<64>), dim3((unsigned)prep_blocks), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(o), p.dout, lse, workspace, workspace + rows, rows);
+    else if (d == 128)
+        hipLaunchKernelGGL((attn_bwd_prep_kernel<128>), dim3((unsigned)prep_blocks), dim3(256), 0, st,
+                           static_cast<const uint16_t*>(o), p.dout, lse, workspace, workspace + rows, rows);
+    else
+        return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (d == 64) return causal ? launch_main<64, true>(p, st) : launch_main<64, false>(p, st);
+    return causal ? launch_main<128, true>(p, st) : launch_main<128, false>(p, st);
+}
+
+}  // namespace mi355

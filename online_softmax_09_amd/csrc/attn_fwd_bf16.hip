@@ -10,13 +10,13 @@
 //
 // gfx950 mapping (a design of its own, not the pages' warp/shared-memory scheme):
 //
-//   * Block = 4 wavefronts = 128 query rows; each wavefront owns 32 query rows for
-//     the whole key loop.  Key tiles are 64 keys.
+//   * Block = 8 wavefronts = 256 query rows; each wavefront owns 32 query rows for
+//     the whole key loop.  Key tiles are 64 keys.  Waves w and w + 4 share a SIMD.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     A = a 32-key slice of K (from LDS), B = Q^T (held in registers for the whole
 //     loop).  In the 32x32 accumulator, lane l holds one column, i.e. one query row
 //     (l mod 32), and 16 of its keys; the other 16 keys of that row sit in lane l^32.
-//     So the row max is 31 in-lane maxima plus one exchange, and the row sum needs no
+//     So the row max is in-lane maxima plus one exchange, and the row sum needs no
 //     exchange at all until the end (each half keeps a partial l under the same m).
 //   * The output is accumulated transposed too, O^T += V^T P^T: the B operand
 //     (P^T, 8 keys x 1 query per lane) is exactly what the lane already holds after
@@ -26,15 +26,16 @@
 //     8+4h..8+4h+3 of a 16-key group) of its output column, the order in which the
 //     S^T accumulator hands P to the lanes.  The O^T accumulator keeps one query row
 //     per lane as well, so alpha rescales it with no exchange.
-//   * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4: each lane's
-//     16 bytes land at base + 16 * lane), with no registers and no LDS write
+//   * K and V tiles go from HBM straight into LDS (buffer_load_dwordx4 ... lds: each
+//     lane's 16 bytes land at base + 16 * lane), with no registers and no LDS write
 //     instructions.  The rows are unpadded and each row's 16-byte chunks are stored
 //     XOR-permuted, a permutation chosen so that the 16-byte K reads and the
 //     transposing V reads are free of LDS bank conflicts; a lane fetches the chunk
 //     that belongs at its LDS position.
-//   * Software pipeline, three tiles deep: while the matrix cores compute O += P V of
-//     the previous tile and then S of the next tile, the vector ALUs run this tile's
-//     softmax, interleaved instruction by instruction (sched_group_barrier).
+//   * Ping-pong between the two wavefronts of each SIMD: the work on a tile is split
+//     into a matrix part (P V of the previous tile, then S of the next) and a vector
+//     part (this tile's softmax), and the two groups of four wavefronts run opposite
+//     parts in each half-step, separated by block barriers.
 //   * The row's reference maximum m moves lazily: only when a tile's maximum exceeds
 //     it by more than 2^8 (kLazy).  Until then alpha is exactly 1 and the rescale of O
 //     is skipped (decided per wavefront); P stays at most 2^8.  The result O / l and
@@ -49,21 +50,10 @@
 
 #include "device_common.hpp"
 #include "launchers.hpp"
+#include "mfma_bf16.hpp"
 
 namespace mi355 {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Word 3 of a raw (unformatted, byte-addressed) buffer resource on gfx9.
-constexpr int kBufferWord3 = 0x00020000;
 
 constexpr int kWaves = 8;                  // two groups of four, one of each per SIMD
 constexpr int kThreads = 64 * kWaves;
@@ -71,13 +61,6 @@ constexpr int kGroupThreads = kThreads / 2;
 constexpr int kBM = 32 * kWaves;           // query rows per block
 constexpr int kRoundBytes = 16 * kGroupThreads;  // bytes one group-wide 16-byte copy moves
 constexpr int kBN = 64;           // keys per tile
-
-// Two floats to two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
 
 // The reference maximum of a row moves only when a tile's maximum exceeds it by more
 // than this many powers of two; until then the probabilities exp2(c s - m) stay at
@@ -113,12 +96,6 @@ struct Params {
     float scale_log2;  // |scale| * log2(e)
     int negate_q;      // scale < 0
 };
-
-// Transposing LDS load: within each group of 16 lanes, lane i receives element i % 4
-// of the 8-byte blocks addressed by lanes i / 4 + 4 k, k = 0..3.
-__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const lds_char*)(p));
-}
 
 // One tile of K or V from HBM straight to LDS, by one group of kGroupThreads threads.
 // Thread t of the group writes LDS bytes

@@ -27,4 +27,9 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int N, int d, float scale, bool causal, hipStream_t st);
 
+// workspace: 2 * B * H * N floats (per-row D, then LSE * log2(e)).
+hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,
+                                int N, int d, float scale, bool causal, hipStream_t st);
+
 }  // namespace mi355

@@ -95,3 +95,37 @@ def test_softmax_argument_checks(lib):
     assert f(A, A + 16, 4, 16, None) == INVALID   # partial overlap
     assert f(A, Bp, 4, (1 << 20) + 1, None) == UNSUPPORTED
     assert f(A, Bp, 1 << 31, 4, None) == UNSUPPORTED
+
+
+# More fake addresses for the gradient entry point.
+F, G, Hp, I, J = (0x100000000 * (i + 6) for i in range(5))
+
+
+def _bwd(lib, q=A, k=Bp, v=C, o=D, do=F, lse=E, dq=G, dk=Hp, dv=I, ws=J, B=1, H=1, N=16, d=64, scale=0.125,
+         causal=0):
+    return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, N, d, scale, causal, None)
+
+
+def test_backward_argument_checks(lib):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert _bwd(lib, **{name: None}) == INVALID, name
+    for bad in (dict(B=0), dict(H=0), dict(N=0), dict(d=0)):
+        assert _bwd(lib, **bad) == INVALID, bad
+    for s in (math.inf, math.nan):
+        assert _bwd(lib, scale=s) == INVALID
+    assert _bwd(lib, causal=-1) == INVALID
+    for name, addr in (("do", F), ("dq", G), ("dk", Hp), ("dv", I), ("ws", J)):
+        assert _bwd(lib, **{name: addr + 8}) == INVALID, name  # misaligned
+    assert _bwd(lib, dq=A + 32) == INVALID    # dq overlaps q
+    assert _bwd(lib, dk=F) == INVALID         # dk overlaps dout
+    assert _bwd(lib, dv=G + 16) == INVALID    # dv overlaps dq
+    assert _bwd(lib, ws=E) == INVALID         # workspace overlaps lse
+    for d in (32, 96, 256):
+        assert _bwd(lib, d=d) == UNSUPPORTED, d
+
+
+def test_backward_workspace_size(lib):
+    assert lib.fa_bwd_workspace_bytes(2, 32, 8192) == 2 * 32 * 8192 * 8
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1) == 8
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1) == -1
+    assert lib.fa_bwd_workspace_bytes(1, 1, -5) == -1

@@ -91,6 +91,13 @@ def attention_inputs(B, H, N, d, seed, dtype="bf16", k_outlier_frac=0.0,
     return _to_torch(q, dtype), _to_torch(k, dtype), _to_torch(v, dtype)
 
 
+def upstream_grad(B, H, N, d, seed, dtype="bf16"):
+    """An upstream gradient dL/dO as a CPU torch tensor [B, H, N, d]: iid N(0, 1) drawn
+    from its own stream (seed + 31), so it never repeats Q, K or V of the same seed."""
+    g = generator(seed + 31)
+    return _to_torch(g.standard_normal((B, H, N, d), dtype=np.float32), dtype)
+
+
 def attention_inputs_for(name):
     c = CONFIGS[name]
     return attention_inputs(c["B"], c["H"], c["N"], c["d"], c["seed"], c["dtype"],
