@@ -16,6 +16,9 @@ Prints ONE JSON line:
   cpu_baseline       the float64 oracle on whole heads of the same attention workload, timed on
                      the host (about 10-30 s), in the same TFLOP/s convention
   parity     max abs error of the GPU output on the heads the oracle evaluated
+  next       kernels beyond the hot path, timed after it on the same inputs (not part of the
+             step): attn_bwd = fa_bwd on the attention workload, in TFLOP/s counted as 2.5x
+             the forward's flops (the five matrix products of the gradients)
 
 Only the cpu_baseline leg imports the oracle.
 """
@@ -44,7 +47,7 @@ CSRC = os.path.join(ROOT, "online_softmax_09_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 # kernel-name prefix in rocprofv3 output -> sources whose hash stamps its counters
 KERNEL_SOURCES = {
-    "attn_fwd_bf16": ["attn_fwd_bf16.hip", "device_common.hpp"],
+    "attn_fwd_bf16": ["attn_fwd_bf16.hip", "device_common.hpp", "mfma_bf16.hpp"],
     "softmax_rows": ["softmax_rows.hip", "device_common.hpp"],
 }
 
@@ -171,6 +174,36 @@ def cpu_baseline(q, k, v, scale, causal, o_gpu, lse_gpu, budget_s):
         "lse_max_abs": err_l, "o_tol": 2e-2, "lse_tol": 1e-2}
 
 
+def time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale, steps, warmup):
+    """fa_bwd on the attention workload (O and LSE from fa_fwd, a seeded upstream gradient),
+    timed with HIP events per launch."""
+    B, H, N, d, causal = ca["B"], ca["H"], ca["N"], ca["d"], ca["causal"]
+    do = workloads.upstream_grad(B, H, N, d, seed=ca["seed"]).to(dev)
+    dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+    ws = torch.empty(B * H * N * 2, dtype=torch.float32, device=dev)
+
+    def run():
+        osm.fa_bwd(qd, kd, vd, od, lsed, do, scale=scale, causal=causal, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    fl = 2.5 * attn_flops(B, H, N, d, causal)
+    avg = float(np.mean(ms))
+    tf = fl / (avg * 1e-3) / 1e12
+    return {"workload": ATTN, "ms_mean": round(avg, 4), "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4),
+            "launches": steps, "flops_per_launch": fl, "tflops": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,7 +211,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
-    ap.add_argument("--only", choices=["attn", "softmax"], default=None,
+    ap.add_argument("--no-next", action="store_true", help="skip the kernels beyond the hot path")
+    ap.add_argument("--only", choices=["attn", "softmax", "bwd"], default=None,
                     help="time one kernel only (for profiler runs; not the bench line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
@@ -225,6 +259,11 @@ def main():
 
     run_attn = args.only in (None, "attn")
     run_sm = args.only in (None, "softmax")
+    if args.only == "bwd":
+        osm.fa_fwd(qd, kd, vd, scale=scale, causal=causal, out=od, lse=lsed)
+        r = time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale, args.steps, args.warmup)
+        print(json.dumps({"only": "bwd", **r}))
+        return
 
     def step(ev=None):
         if run_attn:
@@ -286,6 +325,11 @@ def main():
         o_cpu, lse_cpu = od.cpu(), lsed.cpu()
         cpu, parity = cpu_baseline(q, k, v, scale, causal, o_cpu, lse_cpu, args.cpu_budget)
 
+    nxt = None
+    if not args.no_next:
+        nxt = {"attn_bwd": time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale,
+                                    min(args.steps, 10), 2)}
+
     traffic = read_traffic()
     line = {
         "metric": "attn fwd TFLOP/s & % bf16 MFMA peak (causal N=8192 d=128); softmax GB/s",
@@ -319,6 +363,7 @@ def main():
                              "traffic_algorithmic": sm_bytes},
         "cpu_baseline": cpu,
         "parity": parity,
+        "next": nxt,
         "timing": {"method": "HIP events on the launch stream", "l2_flush": False,
                    "wall_s_timed_region": round(wall, 3), "input_gen_s": round(t_gen, 1)},
         "inputs_sha256_16": hashes,
