@@ -17,6 +17,9 @@ fp32 / bf16 inputs, by the plain definition of the operation:
   softmax by the same three passes, ``O = P V`` and ``LSE = m + ln l``.
 * ``attention_bwd`` — the gradients dQ, dK, dV of that definition for an upstream dO,
   by the chain rule with S, P, dP and dS materialised.
+* ``attention_split`` — the same definition for N_q queries against N_k keys (causal
+  masks bottom-right aligned), and the log-domain merge of partial (O, LSE) results over
+  disjoint key sets.
 
 Pages cited (titles as they appear on the pages; section numbers are the pages'):
 
@@ -46,3 +49,4 @@ from .softmax import (  # noqa: F401
 )
 from .attention import attention, attention_rows  # noqa: F401
 from .attention_bwd import attention_backward  # noqa: F401
+from .attention_split import attention_rect, merge_attention_states, split_bounds  # noqa: F401
