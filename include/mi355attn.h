@@ -20,6 +20,9 @@
  *   Attention gradients (fa_bwd), same page, section 7.2: dQ, dK, dV of the forward,
  *   recomputing the probabilities tile by tile from the saved per-row LSE.
  *
+ *   Split-KV forward and merge (fa_fwd_splitkv, attn_merge_states), same page, section
+ *   4.1: partial results over parts of the keys combined with the online-softmax merge.
+ *
  * Conventions shared by every entry point:
  *
  *   Memory     All pointers are device pointers to memory owned by the caller.  The
@@ -130,6 +133,51 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 
 /* Bytes of workspace fa_bwd needs for B x H heads of N rows (8 per row); -1 if B, H or N < 1. */
 int64_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * fa_fwd_splitkv — bf16 attention forward for Nq queries against Nk keys, with the keys cut
+ * into n_splits parts whose partial results are merged in the log domain (the shape of
+ * decoding with a key/value cache: Nq small, Nk large).
+ *
+ * Operation: the same attention as fa_fwd, O = softmax(scale * Q K^T) V and LSE, over
+ * rectangular Q [Nq] x K [Nk].  Parts are merged by the rescaling rule of "Softmax numerical
+ * stability and IO-aware attention" (zhouzhq2021.github.io), section 4.1, applied to the
+ * normalised partial outputs: LSE = ln sum_p e^{LSE_p}, O = sum_p e^{LSE_p - LSE} O_p.
+ *
+ *   q          [B, H, Nq, d] bf16, read only.
+ *   k, v       [B, H, Nk, d] bf16, read only.
+ *   o          [B, H, Nq, d] bf16, written (rounded once, nearest even).
+ *   lse        [B, H, Nq] float32, written (natural log of the scaled scores' exp-sum).
+ *   workspace  fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits) bytes of device memory,
+ *              16-byte aligned, owned by the caller; overwritten with the partial results
+ *              (float32 [n_splits, B*H*Nq, d], then float32 [n_splits, B*H*Nq]).
+ *   Nq, Nk     >= 1.  causal = 1 needs Nq <= Nk: query i sees keys j <= Nk - Nq + i
+ *              (bottom-right aligned: the queries are the last Nq positions).
+ *   n_splits   1 .. 4096.  Part p covers keys [p*C, (p+1)*C) with C = 64*ceil(ceil(Nk/n_splits)/64);
+ *              trailing parts may be empty.
+ *   d, scale, stream  as for fa_fwd.
+ * o, lse and workspace must not overlap each other or any input.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal, int n_splits, void* stream);
+
+/* Bytes of workspace fa_fwd_splitkv needs: n_splits * B*H*Nq * (d + 1) * 4; -1 on bad sizes. */
+int64_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int d, int n_splits);
+
+/*
+ * attn_merge_states — merges partial attention results computed over disjoint key sets
+ * (for example by other devices, each holding part of the keys), by the rule above.
+ *
+ *   o_parts    [n_parts, rows, d] float32, each part's normalised output, read only.
+ *   lse_parts  [n_parts, rows] float32, each part's LSE (natural log); -inf marks a part with
+ *              no keys for that row, which contributes nothing.  Read only.
+ *   o          [rows, d] bf16, written.   lse  [rows] float32, written.
+ *   n_parts    1 .. 65536.  rows >= 0 (0 does nothing).  d 64 or 128.
+ * A row whose parts all have LSE = -inf has no defined result.  o_parts and o must be 16-byte
+ * aligned, lse_parts and lse 4-byte aligned; outputs must not overlap inputs or each other.
+ */
+int attn_merge_states(const float* o_parts, const float* lse_parts, void* o, float* lse,
+                      int n_parts, int64_t rows, int d, void* stream);
 
 /* Human-readable name of a return code (static string, never NULL). */
 const char* mi355attn_strerror(int code);

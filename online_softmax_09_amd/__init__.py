@@ -13,13 +13,17 @@ Functions carry the names of the C entry points:
 * ``online_softmax_rows(x)``              float32 [rows, cols] -> softmax of every row
 * ``fa_bwd(q, k, v, o, lse, dout, scale, causal)``  bf16 -> (dq, dk, dv), the gradients
   of ``fa_fwd`` for the upstream gradient ``dout``
+* ``fa_fwd_splitkv(q, k, v, scale, causal, n_splits)``  bf16 q [B, H, Nq, d] against
+  k, v [B, H, Nk, d] -> (o, lse), keys cut into parts merged in the log domain
+* ``attn_merge_states(o_parts, lse_parts)``  float32 partial results -> (o bf16, lse)
 """
 
 import math
 
 from . import _lib
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "online_softmax_rows", "library_path", "version"]
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_fwd_splitkv", "attn_merge_states", "online_softmax_rows",
+           "library_path", "version"]
 
 
 def library_path():
@@ -130,6 +134,76 @@ def fa_bwd(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, dk=None, dv
                         B, H, N, d, float(scale), 1 if causal else 0, _stream_handle(stream, q.device))
     _lib.check(rc, "fa_bwd")
     return tuple(grads)
+
+
+def _check_gpu_tensor(name, t, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} GPU tensor")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=1, out=None, lse=None, workspace=None,
+                   stream=None):
+    """bf16 attention of q [B, H, Nq, d] against k, v [B, H, Nk, d] with the keys cut into
+    n_splits parts merged in the log domain; returns (o, lse).  Causal masks are
+    bottom-right aligned (query i sees keys j <= Nk - Nq + i)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_gpu_tensor(name, t, torch.bfloat16, 4)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape or k.device != q.device or v.device != q.device:
+        raise ValueError("k and v must be [B, H, Nk, d] on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check_gpu_tensor("out", out, torch.bfloat16, 4)
+    _check_gpu_tensor("lse", lse, torch.float32, 3)
+    if out.shape != q.shape or lse.shape != (B, H, Nq):
+        raise ValueError("out must be like q and lse [B, H, Nq]")
+    lib = _lib.load()
+    need = lib.fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, int(n_splits))
+    if need < 0:
+        raise ValueError("bad sizes")
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or not workspace.is_contiguous() or workspace.numel() * 4 < need:
+        raise ValueError(f"workspace must be a contiguous float32 tensor of at least {need} bytes")
+    with torch.cuda.device(q.device):
+        rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                workspace.data_ptr(), B, H, Nq, Nk, d, float(scale), 1 if causal else 0,
+                                int(n_splits), _stream_handle(stream, q.device))
+    _lib.check(rc, "fa_fwd_splitkv")
+    return out, lse
+
+
+def attn_merge_states(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """Merge float32 partial results o_parts [P, rows, d], lse_parts [P, rows] (natural
+    log, -inf = empty part) into (o bf16 [rows, d], lse float32 [rows])."""
+    torch = _torch()
+    _check_gpu_tensor("o_parts", o_parts, torch.float32, 3)
+    _check_gpu_tensor("lse_parts", lse_parts, torch.float32, 2)
+    P, rows, d = o_parts.shape
+    if lse_parts.shape != (P, rows) or lse_parts.device != o_parts.device:
+        raise ValueError("lse_parts must be [P, rows] on o_parts' device")
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((rows,), dtype=torch.float32, device=o_parts.device)
+    _check_gpu_tensor("out", out, torch.bfloat16, 2)
+    _check_gpu_tensor("lse", lse, torch.float32, 1)
+    if out.shape != (rows, d) or lse.shape != (rows,):
+        raise ValueError("out must be [rows, d] and lse [rows]")
+    with torch.cuda.device(o_parts.device):
+        rc = _lib.load().attn_merge_states(o_parts.data_ptr(), lse_parts.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                           P, rows, d, _stream_handle(stream, o_parts.device))
+    _lib.check(rc, "attn_merge_states")
+    return out, lse
 
 
 def online_softmax_rows(x, out=None, stream=None):

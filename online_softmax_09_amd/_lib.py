@@ -24,6 +24,9 @@ SIGNATURES = {
     "online_softmax_rows": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp]),
     "fa_bwd": (_c_int, [_vp] * 10 + [_c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
     "fa_bwd_workspace_bytes": (_c_i64, [_c_int, _c_int, _c_int]),
+    "fa_fwd_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 5 + [_c_f, _c_int, _c_int, _vp]),
+    "fa_fwd_splitkv_workspace_bytes": (_c_i64, [_c_int] * 5),
+    "attn_merge_states": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_i64, _c_int, _vp]),
     "mi355attn_strerror": (ctypes.c_char_p, [_c_int]),
     "mi355attn_last_hip_error": (_c_int, []),
     "mi355attn_version": (_c_int, []),

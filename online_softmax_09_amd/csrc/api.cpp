@@ -107,6 +107,61 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                                               H, N, d, scale, causal != 0, static_cast<hipStream_t>(stream)));
 }
 
+int64_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int d, int n_splits) {
+    if (B < 1 || H < 1 || Nq < 1 || d < 1 || n_splits < 1) return -1;
+    return (int64_t)n_splits * B * H * Nq * (int64_t)(d + 1) * (int64_t)sizeof(float);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace, int B, int H,
+                   int Nq, int Nk, int d, float scale, int causal, int n_splits, void* stream) {
+    if (!q || !k || !v || !o || !lse || !workspace) return MI355ATTN_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return MI355ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return MI355ATTN_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return MI355ATTN_ERR_INVALID_ARG;
+    if (causal && Nq > Nk) return MI355ATTN_ERR_INVALID_ARG;
+    if (Nk > INT_MAX - 64) return MI355ATTN_ERR_UNSUPPORTED;
+    if (n_splits < 1 || n_splits > 4096) return MI355ATTN_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(workspace))
+        return MI355ATTN_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return MI355ATTN_ERR_UNSUPPORTED;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    if (bh * (uint64_t)((Nq + 31) / 32) * (uint64_t)n_splits > (uint64_t)INT_MAX) return MI355ATTN_ERR_UNSUPPORTED;
+    if (bh * (uint64_t)Nq > (uint64_t)INT_MAX) return MI355ATTN_ERR_UNSUPPORTED;
+    const uint64_t qb = bh * Nq * d * 2, kb = bh * Nk * d * 2, lb = bh * Nq * 4;
+    const uint64_t wb = (uint64_t)fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits);
+    const void* outs[3] = {o, lse, workspace};
+    const uint64_t out_bytes[3] = {qb, lb, wb};
+    const void* ins[3] = {q, k, v};
+    const uint64_t in_bytes[3] = {qb, kb, kb};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return MI355ATTN_ERR_INVALID_ARG;
+        for (int b = 0; b < 3; ++b)
+            if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return MI355ATTN_ERR_INVALID_ARG;
+    }
+    return finish(mi355::launch_attn_splitkv_bf16(q, k, v, o, lse, static_cast<float*>(workspace), B, H, Nq, Nk, d,
+                                                  scale, causal != 0, n_splits, static_cast<hipStream_t>(stream)));
+}
+
+int attn_merge_states(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts, int64_t rows,
+                      int d, void* stream) {
+    if (rows < 0 || n_parts < 1 || n_parts > 65536 || d < 1) return MI355ATTN_ERR_INVALID_ARG;
+    if (rows == 0) return MI355ATTN_OK;
+    if (!o_parts || !lse_parts || !o || !lse) return MI355ATTN_ERR_INVALID_ARG;
+    if (!aligned16(o_parts) || !aligned16(o) || (reinterpret_cast<uintptr_t>(lse_parts) & 3u) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return MI355ATTN_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return MI355ATTN_ERR_UNSUPPORTED;
+    if (rows > (int64_t)INT_MAX) return MI355ATTN_ERR_UNSUPPORTED;
+    const uint64_t pb = (uint64_t)n_parts * rows * d * 4, plb = (uint64_t)n_parts * rows * 4;
+    const uint64_t ob = (uint64_t)rows * d * 2, lb = (uint64_t)rows * 4;
+    if (overlaps(o, ob, lse, lb) || overlaps(o, ob, o_parts, pb) || overlaps(o, ob, lse_parts, plb) ||
+        overlaps(lse, lb, o_parts, pb) || overlaps(lse, lb, lse_parts, plb))
+        return MI355ATTN_ERR_INVALID_ARG;
+    return finish(mi355::launch_attn_merge(o_parts, lse_parts, o, lse, n_parts, rows, d,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int online_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream) {
     if (rows < 0 || cols < 1) return MI355ATTN_ERR_INVALID_ARG;
     if (rows == 0) return MI355ATTN_OK;

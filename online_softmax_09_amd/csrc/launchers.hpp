@@ -27,6 +27,17 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int N, int d, float scale, bool causal, hipStream_t st);
 
+// Keys per part of a split-KV call with n_parts parts over Nk keys.
+int64_t splitkv_chunk(int Nk, int n_parts);
+
+// workspace: n_parts * B*H*Nq * (d + 1) floats (partial outputs, then partial LSE).
+hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    float* workspace, int B, int H, int Nq, int Nk, int d, float scale, bool causal,
+                                    int n_parts, hipStream_t st);
+
+hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts,
+                             int64_t rows, int d, hipStream_t st);
+
 // workspace: 2 * B * H * N floats (per-row D, then LSE * log2(e)).
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                 const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,

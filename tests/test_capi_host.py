@@ -129,3 +129,40 @@ def test_backward_workspace_size(lib):
     assert lib.fa_bwd_workspace_bytes(1, 1, 1) == 8
     assert lib.fa_bwd_workspace_bytes(0, 1, 1) == -1
     assert lib.fa_bwd_workspace_bytes(1, 1, -5) == -1
+
+
+def _skv(lib, q=A, k=Bp, v=C, o=D, lse=E, ws=F, B=1, H=2, Nq=3, Nk=100, d=128, scale=0.1, causal=1, n=4):
+    return lib.fa_fwd_splitkv(q, k, v, o, lse, ws, B, H, Nq, Nk, d, scale, causal, n, None)
+
+
+def test_splitkv_argument_checks(lib):
+    for name in ("q", "k", "v", "o", "lse", "ws"):
+        assert _skv(lib, **{name: None}) == INVALID, name
+    for bad in (dict(B=0), dict(H=0), dict(Nq=0), dict(Nk=0), dict(d=0), dict(n=0), dict(n=4097),
+                dict(causal=2), dict(Nq=101, Nk=100)):
+        assert _skv(lib, **bad) == INVALID, bad
+    assert _skv(lib, scale=math.nan) == INVALID
+    assert _skv(lib, ws=F + 4) == INVALID             # misaligned
+    assert _skv(lib, o=A + 16) == INVALID             # o overlaps q
+    assert _skv(lib, ws=Bp + 32) == INVALID           # workspace overlaps k
+    assert _skv(lib, lse=D + 32) == INVALID           # lse overlaps o
+    assert _skv(lib, d=96) == UNSUPPORTED
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 128, 4) == 4 * 6 * 129 * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 128, 0) == -1
+
+
+def test_merge_argument_checks(lib):
+    f = lib.attn_merge_states
+    assert f(A, Bp, C, D, 4, 0, 128, None) == OK          # no rows: nothing to do
+    assert f(None, Bp, C, D, 4, 8, 128, None) == INVALID
+    assert f(A, None, C, D, 4, 8, 128, None) == INVALID
+    assert f(A, Bp, None, D, 4, 8, 128, None) == INVALID
+    assert f(A, Bp, C, None, 4, 8, 128, None) == INVALID
+    assert f(A, Bp, C, D, 0, 8, 128, None) == INVALID
+    assert f(A, Bp, C, D, 65537, 8, 128, None) == INVALID
+    assert f(A, Bp, C, D, 4, -1, 128, None) == INVALID
+    assert f(A + 4, Bp, C, D, 4, 8, 128, None) == INVALID  # o_parts misaligned
+    assert f(A, Bp + 2, C, D, 4, 8, 128, None) == INVALID  # lse_parts misaligned
+    assert f(A, Bp, A + 64, D, 4, 8, 128, None) == INVALID  # o overlaps o_parts
+    assert f(A, Bp, C, Bp, 4, 8, 128, None) == INVALID     # lse overlaps lse_parts
+    assert f(A, Bp, C, D, 4, 8, 32, None) == UNSUPPORTED

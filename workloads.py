@@ -50,6 +50,13 @@ CONFIGS = {
                                              d=128, causal=True, seed=SEED_BASE + 4,
                                              k_outlier_frac=0.001, k_outlier_scale=8.0,
                                              sample_rows=1024),
+    # Decoding against a key/value cache: the long causal workload's heads with one new
+    # query each (bottom-right aligned), keys cut into parts merged in the log domain.
+    "decode_bf16_b1h8q1k131072d128": dict(kind="decode", dtype="bf16", B=1, H=8, Nq=1, Nk=131072,
+                                          d=128, causal=True, n_splits=256, seed=SEED_BASE + 5),
+    # A batch of decoding streams with 16 queries each (speculative or chunked decoding).
+    "decode_bf16_b4h32q16k32768d128": dict(kind="decode", dtype="bf16", B=4, H=32, Nq=16, Nk=32768,
+                                           d=128, causal=True, n_splits=32, seed=SEED_BASE + 6),
 }
 
 
@@ -96,6 +103,36 @@ def upstream_grad(B, H, N, d, seed, dtype="bf16"):
     from its own stream (seed + 31), so it never repeats Q, K or V of the same seed."""
     g = generator(seed + 31)
     return _to_torch(g.standard_normal((B, H, N, d), dtype=np.float32), dtype)
+
+
+def decode_inputs(B, H, Nq, Nk, d, seed, dtype="bf16"):
+    """q [B, H, Nq, d] and k, v [B, H, Nk, d] as CPU torch tensors, iid N(0, 1)."""
+    g = generator(seed)
+    q = g.standard_normal((B, H, Nq, d), dtype=np.float32)
+    k = g.standard_normal((B, H, Nk, d), dtype=np.float32)
+    v = g.standard_normal((B, H, Nk, d), dtype=np.float32)
+    return _to_torch(q, dtype), _to_torch(k, dtype), _to_torch(v, dtype)
+
+
+def decode_inputs_for(name):
+    c = CONFIGS[name]
+    return decode_inputs(c["B"], c["H"], c["Nq"], c["Nk"], c["d"], c["seed"], c["dtype"])
+
+
+def merge_parts(n_parts, rows, d, seed, empty_frac=0.1):
+    """Partial results for the merge: o_parts [n_parts, rows, d] float32 N(0, 1) and
+    lse_parts [n_parts, rows] float32 N(0, sd 3), with a seeded share of parts marked
+    empty (-inf; never all parts of a row) and the last row's LSE shifted by +1000."""
+    import torch
+
+    g = generator(seed)
+    o = g.standard_normal((n_parts, rows, d), dtype=np.float32)
+    lse = (g.standard_normal((n_parts, rows)) * 3.0).astype(np.float32)
+    empty = g.random((n_parts, rows)) < empty_frac
+    empty[0] = False
+    lse[empty] = -np.inf
+    lse[:, -1] += np.float32(1000.0)
+    return torch.from_numpy(o), torch.from_numpy(lse)
 
 
 def attention_inputs_for(name):
