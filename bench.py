@@ -18,7 +18,9 @@ Prints ONE JSON line:
   parity     max abs error of the GPU output on the heads the oracle evaluated
   next       kernels beyond the hot path, timed after it on the same inputs (not part of the
              step): attn_bwd = fa_bwd on the attention workload, in TFLOP/s counted as 2.5x
-             the forward's flops (the five matrix products of the gradients)
+             the forward's flops (the five matrix products of the gradients); decode_* =
+             fa_fwd_splitkv on the decoding workloads, in GB/s of algorithmic HBM traffic
+             (K and V once, plus Q, O and LSE) against the HBM3E peak
 
 Only the cpu_baseline leg imports the oracle.
 """
@@ -204,6 +206,44 @@ def time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale, steps,
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def time_decode(osm, workloads, torch, dev, name, steps, warmup):
+    """fa_fwd_splitkv on a decoding workload, timed with HIP events per call."""
+    c = workloads.CONFIGS[name]
+    B, H, Nq, Nk, d = c["B"], c["H"], c["Nq"], c["Nk"], c["d"]
+    q, k, v = (t.to(dev) for t in workloads.decode_inputs_for(name))
+    scale = workloads.default_scale(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    need = osm._lib.load().fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, c["n_splits"])
+    ws = torch.empty(need // 4, dtype=torch.float32, device=dev)
+
+    def run():
+        osm.fa_fwd_splitkv(q, k, v, scale=scale, causal=c["causal"], n_splits=c["n_splits"], out=o, lse=lse,
+                           workspace=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    algo = 2.0 * B * H * Nk * d * 2 + 2.0 * B * H * Nq * d * 2 + 4.0 * B * H * Nq
+    gbps = algo / (avg * 1e-3) / 1e9
+    return {"workload": name, "n_splits": c["n_splits"], "ms_mean": round(avg, 4), "ms_min": round(min(ms), 4),
+            "ms_max": round(max(ms), 4), "launches": steps, "bytes_algorithmic": algo, "gbps": round(gbps, 1),
+            "workspace_bytes": need,
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+
+
+DECODE = ["decode_bf16_b1h8q1k131072d128", "decode_bf16_b4h32q16k32768d128"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,7 +252,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--no-next", action="store_true", help="skip the kernels beyond the hot path")
-    ap.add_argument("--only", choices=["attn", "softmax", "bwd"], default=None,
+    ap.add_argument("--only", choices=["attn", "softmax", "bwd", "decode"], default=None,
                     help="time one kernel only (for profiler runs; not the bench line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
@@ -259,6 +299,10 @@ def main():
 
     run_attn = args.only in (None, "attn")
     run_sm = args.only in (None, "softmax")
+    if args.only == "decode":
+        print(json.dumps({"only": "decode", "runs": [time_decode(osm, workloads, torch, dev, n, args.steps,
+                                                                   args.warmup) for n in DECODE]}))
+        return
     if args.only == "bwd":
         osm.fa_fwd(qd, kd, vd, scale=scale, causal=causal, out=od, lse=lsed)
         r = time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale, args.steps, args.warmup)
@@ -329,6 +373,8 @@ def main():
     if not args.no_next:
         nxt = {"attn_bwd": time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale,
                                     min(args.steps, 10), 2)}
+        for n in DECODE:
+            nxt[n] = time_decode(osm, workloads, torch, dev, n, min(args.steps, 20), 3)
 
     traffic = read_traffic()
     line = {

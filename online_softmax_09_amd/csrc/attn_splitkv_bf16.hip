@@ -12,16 +12,20 @@
 //
 // Partial kernel (gfx950): one wavefront per block and per (head, 32-query tile, part).
 // With one or a few queries the work is a stream over the key/value cache, bound by
-// HBM; each wavefront keeps its own ring of three 32-key K and V sub-tiles in LDS, fed
-// by buffer_load ... lds copies issued two sub-tiles ahead, so a block needs no barrier
-// and several blocks per CU keep enough bytes in flight.  The products are the
+// HBM; each wavefront keeps its own two 32-key K and V sub-tile buffers in LDS (32 KiB at
+// d = 128), fed by buffer_load ... lds copies issued one sub-tile ahead, so a block needs
+// no barrier and five blocks fit a CU, which keeps enough bytes in flight (measured
+// better than deeper rings with fewer blocks).  The products are the
 // forward's: S^T = K Q^T with the Q fragments in registers (one query per lane column;
 // columns past N_q compute garbage and are not stored) and O^T += V^T P^T with V^T read
 // by the transposing LDS load.  The running maximum follows the pages' rule exactly
-// (moved at every sub-tile).
+// (moved at every sub-tile); O is rescaled only when some row's maximum moved.
 //
-// Merge kernel: one block per query row; threads own output columns and walk a share of
-// the parts with the same online rule, then the shares are merged through LDS.
+// Merge kernel: one block per query row (1024 threads when there are few rows, else
+// 256); threads own output columns and a share of the
+// parts.  Each thread takes the maximum LSE of its share, then sums e^{LSE_p - max} O_p
+// and e^{LSE_p - max} over it (independent loads, unrolled), and the shares are merged
+// through LDS with the two-state rule.
 #include "device_common.hpp"
 #include "launchers.hpp"
 #include "mfma_bf16.hpp"
@@ -30,7 +34,7 @@ namespace mi355 {
 namespace {
 
 constexpr int kSK = 32;       // keys per sub-tile (one MFMA row block)
-constexpr int kStages = 3;    // LDS ring depth per wavefront
+constexpr int kStages = 2;    // LDS buffers per wavefront
 constexpr int kQT = 32;       // queries per wavefront
 constexpr int kPartTile = 64; // part boundaries are multiples of this many keys
 
@@ -89,7 +93,7 @@ __device__ __forceinline__ void subtile_to_lds(char* lds, const uint16_t* head, 
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64) void attn_splitkv_partial_kernel(SplitParams p) {
+__global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams p) {
     using L = SLayout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -164,11 +168,11 @@ __global__ __launch_bounds__(64) void attn_splitkv_partial_kernel(SplitParams p)
 
         for (int t = 0; t < n_t; ++t) {
             {
-                const int tn = t + kStages - 1;  // copy two sub-tiles ahead
+                const int tn = t + kStages - 1;  // copy the next sub-tile
                 subtile_to_lds<D, L::K_NP>(k_lds[tn % kStages], kh, lo + tn * kSK, Nk, ck, tn < n_t);
                 subtile_to_lds<D, L::V_NP>(v_lds[tn % kStages], vh, lo + tn * kSK, Nk, cv, tn < n_t);
             }
-            // all but the two newest sub-tiles' copies have landed
+            // every copy but the newest sub-tile's has landed
             __builtin_amdgcn_s_waitcnt(vmcnt_enc((kStages - 1) * 2 * L::ROUNDS));
             const char* kt = k_lds[t % kStages];
             const char* vt = v_lds[t % kStages];
@@ -203,10 +207,12 @@ __global__ __launch_bounds__(64) void attn_splitkv_partial_kernel(SplitParams p)
             }
             l = alpha * l + sum;
             m = m_new;
+            if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-            for (int b = 0; b < DB; ++b)
+                for (int b = 0; b < DB; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+            }
             // O^T += V^T P^T over the two 16-key groups
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
@@ -246,26 +252,24 @@ __global__ __launch_bounds__(64) void attn_splitkv_partial_kernel(SplitParams p)
 }
 
 // ---------------------------------------------------------------------------------
-// Merge: one block of 256 threads per row; thread t owns column t % D of part share
-// t / D and walks parts share, share + G, ... with the online rule.
+// Merge: one block of G * D threads per row; thread t owns column t % D of part share
+// t / D (parts share, share + G, ...).
 // ---------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* o_parts, const float* lse_parts, uint16_t* o,
-                                                         float* lse, int n_parts, int64_t rows) {
-    constexpr int G = 256 / D;
+template <int D, int G>
+__global__ __launch_bounds__(G * D) void attn_merge_kernel(const float* o_parts, const float* lse_parts, uint16_t* o,
+                                                           float* lse, int n_parts, int64_t rows) {
     __shared__ float sm_m[G][D], sm_l[G][D], sm_a[G][D];
     const int64_t row = blockIdx.x;
     const int col = threadIdx.x % D, share = threadIdx.x / D;
-    float m = kNegInf, l = 0.0f, a = 0.0f;  // natural-log state in log2 units: m2 = lse * log2 e
+    float m = kNegInf, l = 0.0f, a = 0.0f;
+    for (int pidx = share; pidx < n_parts; pidx += G) m = fmaxf(m, lse_parts[(int64_t)pidx * rows + row] * kLog2e);
+    const float base = safe_base(m);
+#pragma unroll 8
     for (int pidx = share; pidx < n_parts; pidx += G) {
-        const float lp = lse_parts[(int64_t)pidx * rows + row] * kLog2e;
-        if (lp == kNegInf) continue;  // an empty part is the identity
-        const float m_new = fmaxf(m, lp);
-        const float sc = fast_exp2(m - m_new);  // 0 while m = -inf
-        const float w = fast_exp2(lp - m_new);
-        a = a * sc + w * o_parts[((int64_t)pidx * rows + row) * D + col];
-        l = l * sc + w;
-        m = m_new;
+        const float w = fast_exp2(lse_parts[(int64_t)pidx * rows + row] * kLog2e - base);  // 0 for empty parts
+        const float x = o_parts[((int64_t)pidx * rows + row) * D + col];
+        a = fmaf(w, w > 0.0f ? x : 0.0f, a);
+        l += w;
     }
     sm_m[share][col] = m;
     sm_l[share][col] = l;
@@ -286,11 +290,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* o_parts, c
     }
 }
 
+// Few rows (decoding a handful of streams): 1024 threads per row, so each walks fewer
+// parts; otherwise 256.
 template <int D>
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts,
                         int64_t rows, hipStream_t st) {
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, st, o_parts, lse_parts,
-                       static_cast<uint16_t*>(o), lse, n_parts, rows);
+    if (rows < 1024 && n_parts > 256 / D)
+        hipLaunchKernelGGL((attn_merge_kernel<D, 1024 / D>), dim3((unsigned)rows), dim3(1024), 0, st, o_parts,
+                           lse_parts, static_cast<uint16_t*>(o), lse, n_parts, rows);
+    else
+        hipLaunchKernelGGL((attn_merge_kernel<D, 256 / D>), dim3((unsigned)rows), dim3(256), 0, st, o_parts,
+                           lse_parts, static_cast<uint16_t*>(o), lse, n_parts, rows);
     return hipGetLastError();
 }
 
