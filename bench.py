@@ -20,7 +20,8 @@ Prints ONE JSON line:
              step): attn_bwd = fa_bwd on the attention workload, in TFLOP/s counted as 2.5x
              the forward's flops (the five matrix products of the gradients); decode_* =
              fa_fwd_splitkv on the decoding workloads, in GB/s of algorithmic HBM traffic
-             (K and V once, plus Q, O and LSE) against the HBM3E peak
+             (K and V once, plus Q, O and LSE) against the HBM3E peak; attn_fwd_f16 = fa_fwd_f16
+             on the attention workload's shape in fp16, in TFLOP/s
 
 Only the cpu_baseline leg imports the oracle.
 """
@@ -41,7 +42,7 @@ if ROOT not in sys.path:
 
 ATTN = "attn_bf16_causal_b2h32n8192d128"
 SOFTMAX = "softmax_f32_65536x4096"
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 (and fp16) matrix-core peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E peak
 
 
@@ -244,6 +245,31 @@ def time_decode(osm, workloads, torch, dev, name, steps, warmup):
 DECODE = ["decode_bf16_b1h8q1k131072d128", "decode_bf16_b4h32q16k32768d128"]
 
 
+def time_fwd_f16(osm, workloads, torch, dev, ca, scale, steps, warmup):
+    """fa_fwd_f16 on the attention workload's shape with the same seeded values in fp16."""
+    B, H, N, d, causal = ca["B"], ca["H"], ca["N"], ca["d"], ca["causal"]
+    q, k, v = (t.to(dev) for t in workloads.attention_inputs(B, H, N, d, seed=ca["seed"], dtype="f16"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        osm.fa_fwd_f16(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        osm.fa_fwd_f16(q, k, v, scale=scale, causal=causal, out=o, lse=lse)
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    avg = float(np.mean(ms))
+    fl = attn_flops(B, H, N, d, causal)
+    tf = fl / (avg * 1e-3) / 1e12
+    return {"workload": ATTN.replace("bf16", "f16"), "ms_mean": round(avg, 4), "ms_min": round(min(ms), 4),
+            "launches": steps, "flops_per_launch": fl, "tflops": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -375,6 +401,7 @@ def main():
                                     min(args.steps, 10), 2)}
         for n in DECODE:
             nxt[n] = time_decode(osm, workloads, torch, dev, n, min(args.steps, 20), 3)
+        nxt["attn_fwd_f16"] = time_fwd_f16(osm, workloads, torch, dev, ca, scale, min(args.steps, 20), 3)
 
     traffic = read_traffic()
     line = {

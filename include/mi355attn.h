@@ -83,6 +83,17 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, void* stream);
 
 /*
+ * fa_fwd_f16 — fp16 twin of fa_fwd: q, k, v, o are [B, H, N, d] IEEE binary16; the matrix
+ * products run on fp16 matrix cores with float32 accumulation, P is rounded to fp16 (nearest
+ * even) for P V, and o is rounded once to fp16.  Statistics and lse stay float32.  Arguments,
+ * errors and layout as for fa_fwd.  (The pages contrast fp16 with bf16 and fp32: "Softmax
+ * numerical stability and IO-aware attention", section 6 and question Q3; the agentalpha.top
+ * interview, standard answer point 3, gives fp16 and fp32 error levels.)
+ */
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
  * fa_fwd_f32 — float32 attention forward with the same semantics as fa_fwd.
  *
  *   q, k, v, o  [B, H, N, d] float32;  lse [B, H, N] float32.

@@ -9,6 +9,7 @@ library raises.
 Functions carry the names of the C entry points:
 
 * ``fa_fwd(q, k, v, scale, causal)``      bf16 [B, H, N, d] -> (o bf16, lse float32 [B, H, N])
+* ``fa_fwd_f16(q, k, v, scale, causal)``  the same in fp16
 * ``fa_fwd_f32(q, k, v, scale, causal)``  the same in float32
 * ``online_softmax_rows(x)``              float32 [rows, cols] -> softmax of every row
 * ``fa_bwd(q, k, v, o, lse, dout, scale, causal)``  bf16 -> (dq, dk, dv), the gradients
@@ -22,7 +23,7 @@ import math
 
 from . import _lib
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_fwd_splitkv", "attn_merge_states", "online_softmax_rows",
+__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_fwd_splitkv", "attn_merge_states", "online_softmax_rows",
            "library_path", "version"]
 
 
@@ -94,6 +95,11 @@ def _attention(entry, q, k, v, scale, causal, out, lse, stream, dtype):
 def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
     """bf16 attention forward on the GPU; returns (o, lse).  scale defaults to 1/sqrt(d)."""
     return _attention("fa_fwd", q, k, v, scale, causal, out, lse, stream, _torch().bfloat16)
+
+
+def fa_fwd_f16(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """fp16 attention forward on the GPU; returns (o, lse).  scale defaults to 1/sqrt(d)."""
+    return _attention("fa_fwd_f16", q, k, v, scale, causal, out, lse, stream, _torch().float16)
 
 
 def fa_fwd_f32(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):

@@ -20,6 +20,7 @@ ERR_HIP = -3
 _c_int, _c_i64, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 SIGNATURES = {
     "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
+    "fa_fwd_f16": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
     "fa_fwd_f32": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),
     "online_softmax_rows": (_c_int, [_vp, _vp, _c_i64, _c_i64, _vp]),
     "fa_bwd": (_c_int, [_vp] * 10 + [_c_int, _c_int, _c_int, _c_int, _c_f, _c_int, _vp]),

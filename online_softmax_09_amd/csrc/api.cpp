@@ -65,6 +65,15 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
                                               static_cast<hipStream_t>(stream)));
 }
 
+int fa_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, void* stream) {
+    const int rc = check_attention(q, k, v, o, lse, B, H, N, d, scale, 2);
+    if (rc != MI355ATTN_OK) return rc;
+    if (causal != 0 && causal != 1) return MI355ATTN_ERR_INVALID_ARG;
+    return finish(mi355::launch_attn_fwd_f16(q, k, v, o, lse, B, H, N, d, scale, causal != 0,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                int d, float scale, int causal, void* stream) {
     const int rc = check_attention(q, k, v, o, lse, B, H, N, d, scale, 4);

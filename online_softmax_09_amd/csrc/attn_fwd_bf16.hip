@@ -122,15 +122,16 @@ __device__ __forceinline__ void tile_to_lds(char* lds_tile, const char* head, in
 }
 
 // Per-wavefront state of the key loop and the phases of one key tile.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E>
 struct Wave {
     using L = Layout<D>;
     static constexpr int KS = D / 16;  // k-steps of Q K^T
     static constexpr int DB = D / 32;  // 32-wide blocks of the output dimension
 
-    bf16x8 qf[KS];   // Q^T fragments (B operand of S^T = K Q^T)
+    using v8 = typename E::v8;
+    v8 qf[KS];       // Q^T fragments (B operand of S^T = K Q^T)
     f32x16 acc[DB];  // O^T accumulator: this lane's query row, 16 of each 32 outputs
-    bf16x8 pf[4];    // P^T fragments of the last finished tile (B operand of O^T += V^T P^T)
+    v8 pf[4];        // P^T fragments of the last finished tile (B operand of O^T += V^T P^T)
     int k_off[KS];   // byte offset of this lane's K fragment for k-step ks (row l32)
     int v_off[DB];   // byte offset of this lane's transposing V block for output block b
     float m;         // reference max of |scale| log2(e) score, this lane's row (see kLazy)
@@ -147,8 +148,8 @@ struct Wave {
             f32x16 a = f32x16{};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ktile + 32 * sb * L::RB + k_off[ks]);
-                a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], a, 0, 0, 0);
+                const v8 kf = *reinterpret_cast<const v8*>(ktile + 32 * sb * L::RB + k_off[ks]);
+                a = E::mfma(kf, qf[ks], a);
             }
             st[sb] = a;
         }
@@ -201,8 +202,8 @@ struct Wave {
                 u32x4 w;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    w[t] = pack_bf16x2(st[sb][8 * hb + 2 * t], st[sb][8 * hb + 2 * t + 1]);
-                pf[2 * sb + hb] = __builtin_bit_cast(bf16x8, w);
+                    w[t] = E::pack2(st[sb][8 * hb + 2 * t], st[sb][8 * hb + 2 * t + 1]);
+                pf[2 * sb + hb] = __builtin_bit_cast(v8, w);
             }
     }
 
@@ -229,14 +230,13 @@ struct Wave {
                 const char* pa = vtile + 16 * g * L::RB + v_off[b];
                 const i16x4 lo = lds_read_tr16(pa);
                 const i16x4 hi = lds_read_tr16(pa + 8 * L::RB);
-                const bf16x8 a =
-                    __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[g], acc[b], 0, 0, 0);
+                const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[b] = E::mfma(a, pf[g], acc[b]);
             }
     }
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     using L = Layout<D>;
     constexpr int KS = D / 16;
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     const int k_src = t_row * L::RB + 16 * (t_pos ^ L::k_swz(t_row));
     const int v_src = t_row * L::RB + 16 * (t_pos ^ L::v_swz(t_row));
 
-    Wave<D, CAUSAL> w;
+    Wave<D, CAUSAL, E> w;
     const int l32 = lane & 31;
     w.half = lane >> 5;
     const int my_q = qw0 + l32;
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     for (int s = 0; s < KS; ++s) {
         const u32x4 v4 =
             *reinterpret_cast<const u32x4*>(p.q + head + (int64_t)q_row * D + 16 * s + 8 * w.half);
-        w.qf[s] = __builtin_bit_cast(bf16x8, v4 ^ qsign);
+        w.qf[s] = __builtin_bit_cast(typename E::v8, v4 ^ qsign);
     }
 #pragma unroll
     for (int b = 0; b < DB; ++b) w.acc[b] = f32x16{};
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 u32x2 o2;
-                o2[0] = pack_bf16x2(w.acc[b][4 * i + 0] * inv, w.acc[b][4 * i + 1] * inv);
-                o2[1] = pack_bf16x2(w.acc[b][4 * i + 2] * inv, w.acc[b][4 * i + 3] * inv);
+                o2[0] = E::pack2(w.acc[b][4 * i + 0] * inv, w.acc[b][4 * i + 1] * inv);
+                o2[1] = E::pack2(w.acc[b][4 * i + 2] * inv, w.acc[b][4 * i + 3] * inv);
                 *reinterpret_cast<u32x2*>(orow + 32 * b + 8 * i + 4 * w.half) = o2;
             }
         }
@@ -435,16 +435,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, typename E>
 hipError_t launch(const Params& p, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, E>), dim3((unsigned)p.n_blocks), dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                                int H, int N, int d, float scale, bool causal, hipStream_t st) {
+template <typename E>
+hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                        float scale, bool causal, hipStream_t st) {
     Params p;
     p.q = static_cast<const uint16_t*>(q);
     p.k = static_cast<const uint16_t*>(k);
@@ -457,10 +456,22 @@ hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, voi
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     p.n_blocks = (int)blocks;
     p.scale_log2 = fabsf(scale) * kLog2e;
-    p.negate_q = scale < 0.0f;
-    if (d == 64) return causal ? launch<64, true>(p, st) : launch<64, false>(p, st);
-    if (d == 128) return causal ? launch<128, true>(p, st) : launch<128, false>(p, st);
+    p.negate_q = scale < 0.0f;  // flipping the sign bit negates exactly in bf16 and in fp16
+    if (d == 64) return causal ? launch<64, true, E>(p, st) : launch<64, false, E>(p, st);
+    if (d == 128) return causal ? launch<128, true, E>(p, st) : launch<128, false, E>(p, st);
     return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                int H, int N, int d, float scale, bool causal, hipStream_t st) {
+    return launch_fwd16<ElemBF16>(q, k, v, o, lse, B, H, N, d, scale, causal, st);
+}
+
+hipError_t launch_attn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                               int H, int N, int d, float scale, bool causal, hipStream_t st) {
+    return launch_fwd16<ElemF16>(q, k, v, o, lse, B, H, N, d, scale, causal, st);
 }
 
 }  // namespace mi355

@@ -27,6 +27,10 @@ hipError_t launch_attn_fwd_f32(const float* q, const float* k, const float* v, f
 hipError_t launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int N, int d, float scale, bool causal, hipStream_t st);
 
+// The same kernel on fp16 inputs and output (fp16 matrix products, P rounded to fp16).
+hipError_t launch_attn_fwd_f16(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int N, int d, float scale, bool causal, hipStream_t st);
+
 // Keys per part of a split-KV call with n_parts parts over Nk keys.
 int64_t splitkv_chunk(int Nk, int n_parts);
 

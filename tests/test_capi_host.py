@@ -62,7 +62,7 @@ def _fa(lib, entry, q=A, k=Bp, v=C, o=D, lse=E, B=1, H=1, N=16, d=64, scale=0.12
     return getattr(lib, entry)(q, k, v, o, lse, B, H, N, d, scale, causal, None)
 
 
-@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f16", "fa_fwd_f32"])
 def test_attention_argument_checks(lib, entry):
     assert _fa(lib, entry, q=None) == INVALID
     assert _fa(lib, entry, k=None) == INVALID

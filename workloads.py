@@ -76,6 +76,8 @@ def _to_torch(a, dtype):
     t = torch.from_numpy(np.ascontiguousarray(a))
     if dtype == "bf16":
         t = t.to(torch.bfloat16)  # round-to-nearest-even
+    elif dtype == "f16":
+        t = t.to(torch.float16)   # round-to-nearest-even
     elif dtype != "f32":
         raise ValueError(f"unknown dtype {dtype!r}")
     return t
