@@ -20,6 +20,7 @@ fp32 / bf16 inputs, by the plain definition of the operation:
 * ``attention_split`` — the same definition for N_q queries against N_k keys (causal
   masks bottom-right aligned), and the log-domain merge of partial (O, LSE) results over
   disjoint key sets.
+* ``norms`` — residual add followed by LayerNorm or RMSNorm of rows, by the formulas.
 
 Pages cited (titles as they appear on the pages; section numbers are the pages'):
 
@@ -50,3 +51,4 @@ from .softmax import (  # noqa: F401
 from .attention import attention, attention_rows  # noqa: F401
 from .attention_bwd import attention_backward  # noqa: F401
 from .attention_split import attention_rect, merge_attention_states, split_bounds  # noqa: F401
+from .norms import layer_norm, rms_norm, residual_sum  # noqa: F401
