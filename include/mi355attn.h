@@ -23,6 +23,9 @@
  *   Split-KV forward and merge (fa_fwd_splitkv, attn_merge_states), same page, section
  *   4.1: partial results over parts of the keys combined with the online-softmax merge.
  *
+ *   Fused residual add + RMSNorm / LayerNorm of rows (fused_add_rmsnorm,
+ *   fused_add_layernorm), same page, section 5.
+ *
  * Conventions shared by every entry point:
  *
  *   Memory     All pointers are device pointers to memory owned by the caller.  The
@@ -189,6 +192,32 @@ int64_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int d, int n_splits
  */
 int attn_merge_states(const float* o_parts, const float* lse_parts, void* o, float* lse,
                       int n_parts, int64_t rows, int d, void* stream);
+
+/*
+ * fused_add_rmsnorm / fused_add_layernorm — residual add followed by RMSNorm or LayerNorm of
+ * every row, bf16 in and out, float32 statistics, one pass over memory.
+ *
+ * Operation: "Softmax numerical stability and IO-aware attention" (zhouzhq2021.github.io),
+ * section 5: with h = x + residual (formed in float32),
+ *   RMSNorm    y = h / sqrt(mean(h^2) + eps) * gamma
+ *   LayerNorm  y = (h - mean(h)) / sqrt(var(h) + eps) * gamma + beta,  var = mean((h - mean)^2)
+ * over each row; the variance comes from a stable pairwise (Welford / Chan) combination.
+ *
+ *   x             [rows, cols] bf16, read only.
+ *   residual      [rows, cols] bf16 or NULL (then h = x), read only.
+ *   gamma, beta   [cols] bf16 (beta for LayerNorm only), read only.
+ *   y             [rows, cols] bf16, written (rounded once, nearest even).
+ *   residual_out  [rows, cols] bf16 or NULL: h rounded to bf16 (the updated residual stream).
+ *   rows >= 0 (0 does nothing); cols >= 1 and at most 32768 when cols % 8 == 0 and every
+ *   pointer is 16-byte aligned, else at most 4096 (longer rows: MI355ATTN_ERR_UNSUPPORTED).
+ *   eps finite and >= 0.
+ * Pointers need 2-byte alignment.  y and residual_out may each be exactly x or residual (in
+ * place); no other overlap is allowed.
+ */
+int fused_add_rmsnorm(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
+                      int64_t rows, int64_t cols, float eps, void* stream);
+int fused_add_layernorm(const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                        void* residual_out, int64_t rows, int64_t cols, float eps, void* stream);
 
 /* Human-readable name of a return code (static string, never NULL). */
 const char* mi355attn_strerror(int code);

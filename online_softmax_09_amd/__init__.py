@@ -17,6 +17,8 @@ Functions carry the names of the C entry points:
 * ``fa_fwd_splitkv(q, k, v, scale, causal, n_splits)``  bf16 q [B, H, Nq, d] against
   k, v [B, H, Nk, d] -> (o, lse), keys cut into parts merged in the log domain
 * ``attn_merge_states(o_parts, lse_parts)``  float32 partial results -> (o bf16, lse)
+* ``fused_add_rmsnorm(x, residual, gamma, eps)`` / ``fused_add_layernorm(x, residual, gamma,
+  beta, eps)``  bf16 [rows, cols] -> (y, h = x + residual)
 """
 
 import math
@@ -24,7 +26,7 @@ import math
 from . import _lib
 
 __all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_fwd_splitkv", "attn_merge_states", "online_softmax_rows",
-           "library_path", "version"]
+           "fused_add_rmsnorm", "fused_add_layernorm", "library_path", "version"]
 
 
 def library_path():
@@ -210,6 +212,53 @@ def attn_merge_states(o_parts, lse_parts, out=None, lse=None, stream=None):
                                            P, rows, d, _stream_handle(stream, o_parts.device))
     _lib.check(rc, "attn_merge_states")
     return out, lse
+
+
+def _norm(layer, x, residual, gamma, beta, eps, out, residual_out, stream):
+    torch = _torch()
+    _check_gpu_tensor("x", x, torch.bfloat16, 2)
+    rows, cols = x.shape
+    if residual is not None:
+        _check_gpu_tensor("residual", residual, torch.bfloat16, 2)
+        if residual.shape != x.shape or residual.device != x.device:
+            raise ValueError("residual must be like x")
+    for name, t in (("gamma", gamma), ("beta", beta if layer else None)):
+        if t is None and name == "beta":
+            continue
+        _check_gpu_tensor(name, t, torch.bfloat16, 1)
+        if t.shape != (cols,) or t.device != x.device:
+            raise ValueError(f"{name} must be [cols] on x's device")
+    if out is None:
+        out = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    for name, t in (("out", out), ("residual_out", residual_out)):
+        _check_gpu_tensor(name, t, torch.bfloat16, 2)
+        if t.shape != x.shape or t.device != x.device:
+            raise ValueError(f"{name} must be like x")
+    lib = _lib.load()
+    rp = residual.data_ptr() if residual is not None else None
+    with torch.cuda.device(x.device):
+        if layer:
+            rc = lib.fused_add_layernorm(x.data_ptr(), rp, gamma.data_ptr(), beta.data_ptr(), out.data_ptr(),
+                                         residual_out.data_ptr(), rows, cols, float(eps),
+                                         _stream_handle(stream, x.device))
+        else:
+            rc = lib.fused_add_rmsnorm(x.data_ptr(), rp, gamma.data_ptr(), out.data_ptr(), residual_out.data_ptr(),
+                                       rows, cols, float(eps), _stream_handle(stream, x.device))
+    _lib.check(rc, "fused_add_layernorm" if layer else "fused_add_rmsnorm")
+    return out, residual_out
+
+
+def fused_add_rmsnorm(x, residual, gamma, eps=1e-6, out=None, residual_out=None, stream=None):
+    """RMSNorm of h = x + residual (residual may be None) over the rows of a bf16 [rows, cols]
+    tensor; returns (y, h) in bf16.  out / residual_out may be x or residual (in place)."""
+    return _norm(False, x, residual, gamma, None, eps, out, residual_out, stream)
+
+
+def fused_add_layernorm(x, residual, gamma, beta, eps=1e-5, out=None, residual_out=None, stream=None):
+    """LayerNorm of h = x + residual (residual may be None); returns (y, h) in bf16."""
+    return _norm(True, x, residual, gamma, beta, eps, out, residual_out, stream)
 
 
 def online_softmax_rows(x, out=None, stream=None):

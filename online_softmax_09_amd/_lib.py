@@ -28,6 +28,8 @@ SIGNATURES = {
     "fa_fwd_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 5 + [_c_f, _c_int, _c_int, _vp]),
     "fa_fwd_splitkv_workspace_bytes": (_c_i64, [_c_int] * 5),
     "attn_merge_states": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_i64, _c_int, _vp]),
+    "fused_add_rmsnorm": (_c_int, [_vp] * 5 + [_c_i64, _c_i64, _c_f, _vp]),
+    "fused_add_layernorm": (_c_int, [_vp] * 6 + [_c_i64, _c_i64, _c_f, _vp]),
     "mi355attn_strerror": (ctypes.c_char_p, [_c_int]),
     "mi355attn_last_hip_error": (_c_int, []),
     "mi355attn_version": (_c_int, []),

@@ -171,6 +171,54 @@ int attn_merge_states(const float* o_parts, const float* lse_parts, void* o, flo
                                            static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Shared checks of the two fused normalisations.  beta is checked only for LayerNorm.
+int check_norm(bool layer, const void* x, const void* res, const void* gamma, const void* beta, const void* y,
+               const void* res_out, int64_t rows, int64_t cols, float eps) {
+    if (rows < 0 || cols < 1) return MI355ATTN_ERR_INVALID_ARG;
+    if (!x || !gamma || !y || (layer && !beta)) return MI355ATTN_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || eps < 0.0f) return MI355ATTN_ERR_INVALID_ARG;
+    const void* ptrs[6] = {x, res, gamma, layer ? beta : nullptr, y, res_out};
+    for (const void* q : ptrs)
+        if (q && (reinterpret_cast<uintptr_t>(q) & 1u)) return MI355ATTN_ERR_INVALID_ARG;
+    if (rows > (int64_t)INT_MAX) return MI355ATTN_ERR_UNSUPPORTED;
+    if (cols > mi355::norm_rows_max_cols(layer, x, res, gamma, beta, y, res_out, cols))
+        return MI355ATTN_ERR_UNSUPPORTED;
+    const uint64_t tb = (uint64_t)rows * (uint64_t)cols * 2, vb = (uint64_t)cols * 2;
+    // outputs: identical to an input row buffer is allowed (each element is read before it
+    // is overwritten, by the thread that overwrites it); any other overlap is not
+    auto bad = [&](const void* out, const void* in, uint64_t nin) {
+        return in && out != in && overlaps(out, tb, in, nin);
+    };
+    for (const void* out : {y, res_out}) {
+        if (!out) continue;
+        if (bad(out, x, tb) || bad(out, res, tb) || overlaps(out, tb, gamma, vb) ||
+            (layer && overlaps(out, tb, beta, vb)))
+            return MI355ATTN_ERR_INVALID_ARG;
+    }
+    if (res_out && overlaps(y, tb, res_out, tb)) return MI355ATTN_ERR_INVALID_ARG;
+    return MI355ATTN_OK;
+}
+
+}  // namespace
+
+int fused_add_rmsnorm(const void* x, const void* residual, const void* gamma, void* y, void* residual_out,
+                      int64_t rows, int64_t cols, float eps, void* stream) {
+    const int rc = check_norm(false, x, residual, gamma, nullptr, y, residual_out, rows, cols, eps);
+    if (rc != MI355ATTN_OK || rows == 0) return rc;
+    return finish(mi355::launch_norm_rows(false, x, residual, gamma, nullptr, y, residual_out, rows, cols, eps,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int fused_add_layernorm(const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                        void* residual_out, int64_t rows, int64_t cols, float eps, void* stream) {
+    const int rc = check_norm(true, x, residual, gamma, beta, y, residual_out, rows, cols, eps);
+    if (rc != MI355ATTN_OK || rows == 0) return rc;
+    return finish(mi355::launch_norm_rows(true, x, residual, gamma, beta, y, residual_out, rows, cols, eps,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int online_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream) {
     if (rows < 0 || cols < 1) return MI355ATTN_ERR_INVALID_ARG;
     if (rows == 0) return MI355ATTN_OK;

@@ -42,6 +42,14 @@ hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v,
 hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts,
                              int64_t rows, int d, hipStream_t st);
 
+// Residual add + LayerNorm (layer) or RMSNorm of bf16 rows.  res, beta (RMSNorm) and
+// res_out may be null.  norm_rows_max_cols gives the longest row the launch accepts for
+// these pointers (rows of a multiple of 8 with 16-byte aligned pointers use 16-byte units).
+int64_t norm_rows_max_cols(bool layer, const void* x, const void* res, const void* gamma, const void* beta,
+                           const void* y, const void* res_out, int64_t cols);
+hipError_t launch_norm_rows(bool layer, const void* x, const void* res, const void* gamma, const void* beta, void* y,
+                            void* res_out, int64_t rows, int64_t cols, float eps, hipStream_t st);
+
 // workspace: 2 * B * H * N floats (per-row D, then LSE * log2(e)).
 hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                 const float* lse, void* dq, void* dk, void* dv, float* workspace, int B, int H,

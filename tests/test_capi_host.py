@@ -166,3 +166,23 @@ def test_merge_argument_checks(lib):
     assert f(A, Bp, A + 64, D, 4, 8, 128, None) == INVALID  # o overlaps o_parts
     assert f(A, Bp, C, Bp, 4, 8, 128, None) == INVALID     # lse overlaps lse_parts
     assert f(A, Bp, C, D, 4, 8, 32, None) == UNSUPPORTED
+
+
+def test_norm_argument_checks(lib):
+    rms, ln = lib.fused_add_rmsnorm, lib.fused_add_layernorm
+    assert rms(A, Bp, C, D, E, 0, 64, 1e-5, None) == OK          # no rows: nothing to do
+    assert rms(None, Bp, C, D, E, 4, 64, 1e-5, None) == INVALID
+    assert rms(A, Bp, None, D, E, 4, 64, 1e-5, None) == INVALID
+    assert rms(A, Bp, C, None, E, 4, 64, 1e-5, None) == INVALID
+    assert ln(A, Bp, C, None, D, E, 4, 64, 1e-5, None) == INVALID  # LayerNorm needs beta
+    assert rms(A, Bp, C, D, E, -1, 64, 1e-5, None) == INVALID
+    assert rms(A, Bp, C, D, E, 4, 0, 1e-5, None) == INVALID
+    assert rms(A, Bp, C, D, E, 4, 64, -1.0, None) == INVALID
+    assert rms(A, Bp, C, D, E, 4, 64, math.nan, None) == INVALID
+    assert rms(A + 1, Bp, C, D, E, 4, 64, 1e-5, None) == INVALID  # odd address
+    assert rms(A, Bp, C, A + 64, E, 4, 64, 1e-5, None) == INVALID  # y overlaps x partially
+    assert rms(A, Bp, C, D, D + 64, 4, 64, 1e-5, None) == INVALID  # y overlaps residual_out
+    assert rms(A, Bp, C, C + 2, E, 4, 64, 1e-5, None) == INVALID   # y overlaps gamma
+    assert rms(A, Bp, C, D, E, 4, 32769, 1e-5, None) == UNSUPPORTED
+    assert rms(A, Bp, C, D, E, 4, 4097, 1e-5, None) == UNSUPPORTED  # not a multiple of 8
+    assert rms(A + 2, Bp, C, D, E, 4, 8192, 1e-5, None) == UNSUPPORTED  # 2-byte units only

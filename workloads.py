@@ -57,6 +57,8 @@ CONFIGS = {
     # A batch of decoding streams with 16 queries each (speculative or chunked decoding).
     "decode_bf16_b4h32q16k32768d128": dict(kind="decode", dtype="bf16", B=4, H=32, Nq=16, Nk=32768,
                                            d=128, causal=True, n_splits=16, seed=SEED_BASE + 6),
+    # Residual add + normalisation of 16384 tokens with a hidden size of 8192.
+    "norm_bf16_16384x8192": dict(kind="norm", rows=16384, cols=8192, eps=1e-5, seed=SEED_BASE + 7),
 }
 
 
@@ -135,6 +137,30 @@ def merge_parts(n_parts, rows, d, seed, empty_frac=0.1):
     lse[empty] = -np.inf
     lse[:, -1] += np.float32(1000.0)
     return torch.from_numpy(o), torch.from_numpy(lse)
+
+
+def norm_inputs(rows, cols, seed, special_frac=0.01):
+    """x, residual [rows, cols] and gamma, beta [cols] as bf16 CPU torch tensors.
+
+    x ~ N(0, 1), residual ~ N(0, sd 2); gamma ~ 1 + 0.1 N(0, 1), beta ~ 0.1 N(0, 1).  Seeded
+    disjoint row sets (each special_frac of the rows): rows whose sum h = x + residual is
+    constant (residual = c - x is not representable, so x and residual are both set to the
+    row's first draws), and rows shifted by +1000 in x (a large mean, where a one-pass
+    variance in float32 would cancel).
+    """
+    g = generator(seed)
+    x = g.standard_normal((rows, cols), dtype=np.float32)
+    r = g.standard_normal((rows, cols), dtype=np.float32) * np.float32(2.0)
+    gamma = (1.0 + 0.1 * g.standard_normal(cols)).astype(np.float32)
+    beta = (0.1 * g.standard_normal(cols)).astype(np.float32)
+    n_sp = int(math.floor(special_frac * rows))
+    pick = g.choice(rows, size=2 * n_sp, replace=False)
+    const_rows, shift_rows = np.sort(pick[:n_sp]), np.sort(pick[n_sp:])
+    x[const_rows] = x[const_rows, :1]
+    r[const_rows] = r[const_rows, :1]
+    x[shift_rows] += np.float32(1000.0)
+    t = [_to_torch(a, "bf16") for a in (x, r, gamma, beta)]
+    return t[0], t[1], t[2], t[3], {"constant": const_rows, "plus1000": shift_rows}
 
 
 def attention_inputs_for(name):
