@@ -21,7 +21,9 @@ Prints ONE JSON line:
              the forward's flops (the five matrix products of the gradients); decode_* =
              fa_fwd_splitkv on the decoding workloads, in GB/s of algorithmic HBM traffic
              (K and V once, plus Q, O and LSE) against the HBM3E peak; attn_fwd_f16 = fa_fwd_f16
-             on the attention workload's shape in fp16, in TFLOP/s
+             on the attention workload's shape in fp16, in TFLOP/s; rmsnorm / layernorm =
+             fused_add_rmsnorm / fused_add_layernorm on the 16384 x 8192 bf16 rows, in GB/s of
+             algorithmic traffic (read x and residual, write y and h: 8 bytes per element)
 
 Only the cpu_baseline leg imports the oracle.
 """
@@ -270,6 +272,39 @@ def time_fwd_f16(osm, workloads, torch, dev, ca, scale, steps, warmup):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+NORM = "norm_bf16_16384x8192"
+
+
+def time_norms(osm, workloads, torch, dev, steps, warmup):
+    """fused_add_rmsnorm and fused_add_layernorm on the norm workload, HIP events per call."""
+    c = workloads.CONFIGS[NORM]
+    x, r, g, b, _ = workloads.norm_inputs(c["rows"], c["cols"], c["seed"])
+    x, r, g, b = (t.to(dev) for t in (x, r, g, b))
+    y, h = torch.empty_like(x), torch.empty_like(x)
+    algo = 8.0 * c["rows"] * c["cols"]
+    out = {}
+    for name, run in (("rmsnorm", lambda: osm.fused_add_rmsnorm(x, r, g, eps=c["eps"], out=y, residual_out=h)),
+                      ("layernorm", lambda: osm.fused_add_layernorm(x, r, g, b, eps=c["eps"], out=y,
+                                                                    residual_out=h))):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in evs:
+            e0.record()
+            run()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        avg = float(np.mean(ms))
+        gbps = algo / (avg * 1e-3) / 1e9
+        out[name] = {"workload": NORM, "ms_mean": round(avg, 4), "ms_min": round(min(ms), 4), "launches": steps,
+                     "bytes_algorithmic": algo, "gbps": round(gbps, 1),
+                     "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,7 +313,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--no-next", action="store_true", help="skip the kernels beyond the hot path")
-    ap.add_argument("--only", choices=["attn", "softmax", "bwd", "decode"], default=None,
+    ap.add_argument("--only", choices=["attn", "softmax", "bwd", "decode", "norm"], default=None,
                     help="time one kernel only (for profiler runs; not the bench line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
@@ -325,6 +360,9 @@ def main():
 
     run_attn = args.only in (None, "attn")
     run_sm = args.only in (None, "softmax")
+    if args.only == "norm":
+        print(json.dumps({"only": "norm", **time_norms(osm, workloads, torch, dev, args.steps, args.warmup)}))
+        return
     if args.only == "decode":
         print(json.dumps({"only": "decode", "runs": [time_decode(osm, workloads, torch, dev, n, args.steps,
                                                                    args.warmup) for n in DECODE]}))
@@ -402,6 +440,7 @@ def main():
         for n in DECODE:
             nxt[n] = time_decode(osm, workloads, torch, dev, n, min(args.steps, 20), 3)
         nxt["attn_fwd_f16"] = time_fwd_f16(osm, workloads, torch, dev, ca, scale, min(args.steps, 20), 3)
+        nxt.update(time_norms(osm, workloads, torch, dev, min(args.steps, 20), 3))
 
     traffic = read_traffic()
     line = {
