@@ -373,14 +373,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
         const char* qt = q_lds[cur];
         const char* dt = do_lds[cur];
         const int i0 = i * kT;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-            const int qs0 = i0 + 32 * sb;  // first query of the sub-block
-            // causal: skip sub-blocks whose queries all precede this wave's keys
-            if (!wave_live || (CAUSAL && qs0 + 31 < kw0) || qs0 >= N) continue;
-            const bool masked = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
-            f32x16 s = rows_times_frag<D>(qt, sb, rd, kf);    // S rows = queries
-            f32x16 dp = rows_times_frag<D>(dt, sb, rd, vf);   // dP
+        // P and dS of sub-block sb (rows 32 sb .. 32 sb + 31 of the tile), in place in s, dp
+        auto elementwise = [&](f32x16& s, f32x16& dp, int sb, bool masked) {
+            const int qs0 = i0 + 32 * sb;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE and D vectors
@@ -398,10 +393,38 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
                     dp[r] = pr * (dp[r] - d4[u]);  // dS
                 }
             }
+        };
+        auto accumulate = [&](const f32x16& s, const f32x16& dp, int sb) {
             trans_times_packed<D>(dv, dt, 2 * sb + 0, rd, pack8(s, 0));
             trans_times_packed<D>(dv, dt, 2 * sb + 1, rd, pack8(s, 1));
             trans_times_packed<D>(dk, qt, 2 * sb + 0, rd, pack8(dp, 0));
             trans_times_packed<D>(dk, qt, 2 * sb + 1, rd, pack8(dp, 1));
+        };
+        // Both sub-blocks whole and unmasked: all four score products first, so that the
+        // compiler can run each sub-block's vector work beside the other's matrix
+        // products (explicit interleaving with sched_group_barrier measured slower).
+        const bool full = wave_live && i0 + kT <= N && (!CAUSAL || i0 >= kw0 + 31);
+        if (full) {
+            f32x16 s0 = rows_times_frag<D>(qt, 0, rd, kf);
+            f32x16 dp0 = rows_times_frag<D>(dt, 0, rd, vf);
+            f32x16 s1 = rows_times_frag<D>(qt, 1, rd, kf);
+            f32x16 dp1 = rows_times_frag<D>(dt, 1, rd, vf);
+            elementwise(s0, dp0, 0, false);
+            accumulate(s0, dp0, 0);
+            elementwise(s1, dp1, 1, false);
+            accumulate(s1, dp1, 1);
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                const int qs0 = i0 + 32 * sb;  // first query of the sub-block
+                // causal: skip sub-blocks whose queries all precede this wave's keys
+                if (!wave_live || (CAUSAL && qs0 + 31 < kw0) || qs0 >= N) continue;
+                const bool masked = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
+                f32x16 s = rows_times_frag<D>(qt, sb, rd, kf);    // S rows = queries
+                f32x16 dp = rows_times_frag<D>(dt, sb, rd, vf);   // dP
+                elementwise(s, dp, sb, masked);
+                accumulate(s, dp, sb);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
