@@ -24,6 +24,9 @@ Prints ONE JSON line:
              on the attention workload's shape in fp16, in TFLOP/s; rmsnorm / layernorm =
              fused_add_rmsnorm / fused_add_layernorm on the 16384 x 8192 bf16 rows, in GB/s of
              algorithmic traffic (read x and residual, write y and h: 8 bytes per element)
+  other_configs      the forward on the other attention workloads (bf16 4x16x2048x64
+             non-causal, causal N = 8191, causal 1x8x131072x128 with 0.1% outlier keys;
+             fp32 1x1x256x64 latency), timed the same way
 
 Only the cpu_baseline leg imports the oracle.
 """
@@ -273,6 +276,43 @@ def time_fwd_f16(osm, workloads, torch, dev, ca, scale, steps, warmup):
 
 
 NORM = "norm_bf16_16384x8192"
+OTHER_ATTN = ["attn_bf16_b4h16n2048d64", "attn_bf16_causal_b2h32n8191d128", "attn_bf16_causal_b1h8n131072d128",
+              "attn_f32_b1h1n256d64"]
+
+
+def time_other_configs(osm, workloads, torch, dev, steps, warmup):
+    """fa_fwd (fa_fwd_f32 for the fp32 workload) on the other attention workloads."""
+    out = {}
+    for name in OTHER_ATTN:
+        c = workloads.CONFIGS[name]
+        q, k, v = (t.to(dev) for t in workloads.attention_inputs_for(name))
+        fn = osm.fa_fwd_f32 if c["dtype"] == "f32" else osm.fa_fwd
+        scale = workloads.default_scale(c["d"])
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        n = max(3, steps // 4) if c["N"] > 65536 else steps
+        for _ in range(warmup):
+            fn(q, k, v, scale=scale, causal=c["causal"], out=o, lse=lse)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record()
+            fn(q, k, v, scale=scale, causal=c["causal"], out=o, lse=lse)
+            e1.record()
+        torch.cuda.synchronize()
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        avg = float(np.mean(ms))
+        fl = attn_flops(c["B"], c["H"], c["N"], c["d"], c["causal"])
+        tf = fl / (avg * 1e-3) / 1e12
+        rec = {"ms_mean": round(avg, 4), "ms_min": round(min(ms), 4), "launches": n, "flops_per_launch": fl,
+               "tflops": round(tf, 2)}
+        if c["dtype"] != "f32":
+            rec["frac_of_bf16_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+        else:
+            rec["note"] = "fp32 FMA path, latency bound; no matrix-core roofline"
+        out[name] = rec
+        del q, k, v, o, lse
+    return out
 
 
 def time_norms(osm, workloads, torch, dev, steps, warmup):
@@ -313,7 +353,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--no-next", action="store_true", help="skip the kernels beyond the hot path")
-    ap.add_argument("--only", choices=["attn", "softmax", "bwd", "decode", "norm"], default=None,
+    ap.add_argument("--only", choices=["attn", "softmax", "bwd", "decode", "norm", "other"], default=None,
                     help="time one kernel only (for profiler runs; not the bench line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
@@ -360,6 +400,9 @@ def main():
 
     run_attn = args.only in (None, "attn")
     run_sm = args.only in (None, "softmax")
+    if args.only == "other":
+        print(json.dumps({"only": "other", **time_other_configs(osm, workloads, torch, dev, args.steps, args.warmup)}))
+        return
     if args.only == "norm":
         print(json.dumps({"only": "norm", **time_norms(osm, workloads, torch, dev, args.steps, args.warmup)}))
         return
@@ -434,6 +477,7 @@ def main():
         cpu, parity = cpu_baseline(q, k, v, scale, causal, o_cpu, lse_cpu, args.cpu_budget)
 
     nxt = None
+    other = None
     if not args.no_next:
         nxt = {"attn_bwd": time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale,
                                     min(args.steps, 10), 2)}
@@ -441,6 +485,7 @@ def main():
             nxt[n] = time_decode(osm, workloads, torch, dev, n, min(args.steps, 20), 3)
         nxt["attn_fwd_f16"] = time_fwd_f16(osm, workloads, torch, dev, ca, scale, min(args.steps, 20), 3)
         nxt.update(time_norms(osm, workloads, torch, dev, min(args.steps, 20), 3))
+        other = time_other_configs(osm, workloads, torch, dev, min(args.steps, 20), 2)
 
     traffic = read_traffic()
     line = {
@@ -476,6 +521,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "next": nxt,
+        "other_configs": other,
         "timing": {"method": "HIP events on the launch stream", "l2_flush": False,
                    "wall_s_timed_region": round(wall, 3), "input_gen_s": round(t_gen, 1)},
         "inputs_sha256_16": hashes,
