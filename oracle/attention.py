@@ -11,7 +11,7 @@ Definition followed ([FAM] "the problem starts with the intermediate matrix" and
     O = P V
     LSE_i = m_i + ln l_i         (natural log of sum_j exp(S_ij))
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * ``scale`` is applied to the scores before the softmax; callers pass 1/sqrt(d).
 * Layout is [B, H, N, d] for Q, K, V and O, [B, H, N] for LSE.

@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring): imported by tests and the 
 cpu_baseline leg, never by the GPU library.
 
 ``attention_rect`` is the definition of ``attention`` in oracle/attention.py for N_q
-queries against N_k keys.  Reading taken where the pages are silent (listed in
-the design doc): with causal masking the queries are the last N_q positions of the key
+queries against N_k keys.  Reading taken where the pages are silent: with causal
+masking the queries are the last N_q positions of the key
 sequence (bottom-right alignment, the shape of inference with a key/value cache, which
 [INT] follow-up 3 mentions), so query i sees keys j <= N_k - N_q + i.  With
 N_q = N_k this is the top-left alignment of ``attention``.

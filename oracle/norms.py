@@ -11,7 +11,7 @@ Definitions followed ([SNS] section 5, "the numerical problems of LayerNorm and 
 
 The same section recommends 16-bit inputs and outputs with 32-bit statistics, a stable
 variance algorithm, and fusing the residual add, the normalisation and the type
-conversion into one pass.  Readings taken where it is silent (listed in the design doc): the
+conversion into one pass.  Readings taken where it is silent: the
 fused operation first forms h = x + residual, returns h (the updated residual stream)
 next to y, and normalises h; the variance is the biased one (divided by the row length,
 as in the formula); gamma and beta are per-column vectors.  Here h is the exact sum of
