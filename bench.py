@@ -368,7 +368,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}); the attention heads and softmax rows would shard across "
               f"GPUs with no exchange, but no multi-GPU figure is produced here.", file=sys.stderr)
         sys.exit(2)
