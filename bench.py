@@ -24,6 +24,8 @@ Prints ONE JSON line:
              on the attention workload's shape in fp16, in TFLOP/s; rmsnorm / layernorm =
              fused_add_rmsnorm / fused_add_layernorm on the 16384 x 8192 bf16 rows, in GB/s of
              algorithmic traffic (read x and residual, write y and h: 8 bytes per element)
+  flushed    attention and softmax launch times with L2 and MALL flushed (a 512 MiB device
+             write between calls), next to the unflushed means above
   other_configs      the forward on the other attention workloads (bf16 4x16x2048x64
              non-causal, causal N = 8191, causal 1x8x131072x128 with 0.1% outlier keys;
              fp32 1x1x256x64 latency), timed the same way
@@ -180,6 +182,20 @@ def cpu_baseline(q, k, v, scale, causal, o_gpu, lse_gpu, budget_s):
                    f"three-pass softmax; flops counted as 4 N^2 d / 2 per head"),
     }, {"heads_checked": len(done), "o_max_abs": err_o, "o_max_rel_floor1e-3": rel_o,
         "lse_max_abs": err_l, "o_tol": 2e-2, "lse_tol": 1e-2}
+
+
+def time_flushed(torch, run, calls, flush):
+    """Mean launch time of run() with flush() (a large device write) before every call."""
+    ms = []
+    for _ in range(calls):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return round(float(np.mean(ms)), 4)
 
 
 def time_bwd(osm, workloads, torch, dev, ca, qd, kd, vd, od, lsed, scale, steps, warmup):
@@ -470,6 +486,16 @@ def main():
                           "attn_tflops": tflops, "softmax_gbps": gbps, "steps": args.steps}))
         return
 
+    flush_buf = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flushed = {
+        "attn_ms_mean": time_flushed(torch, lambda: osm.fa_fwd(qd, kd, vd, scale=scale, causal=causal, out=od,
+                                                              lse=lsed), 10, lambda: flush_buf.fill_(1.0)),
+        "softmax_ms_mean": time_flushed(torch, lambda: osm.online_softmax_rows(xd, out=yd), 10,
+                                        lambda: flush_buf.fill_(1.0)),
+        "flush": "512 MiB device write (fill_) before every call",
+    }
+    del flush_buf
+
     cpu = None
     parity = None
     if args.cpu_budget > 0:
@@ -522,6 +548,7 @@ def main():
         "parity": parity,
         "next": nxt,
         "other_configs": other,
+        "flushed": flushed,
         "timing": {"method": "HIP events on the launch stream", "l2_flush": False,
                    "wall_s_timed_region": round(wall, 3), "input_gen_s": round(t_gen, 1)},
         "inputs_sha256_16": hashes,
