@@ -369,7 +369,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--no-next", action="store_true", help="skip the kernels beyond the hot path")
-    ap.add_argument("--only", choices=["attn", "softmax", "bwd", "decode", "norm", "other"], default=None,
+    ap.add_argument("--only", choices=["attn", "softmax", "bwd", "decode", "norm", "other", "f16"], default=None,
                     help="time one kernel only (for profiler runs; not the bench line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
@@ -416,6 +416,10 @@ def main():
 
     run_attn = args.only in (None, "attn")
     run_sm = args.only in (None, "softmax")
+    if args.only == "f16":
+        print(json.dumps({"only": "f16", **time_fwd_f16(osm, workloads, torch, dev, ca, scale, args.steps,
+                                                        args.warmup)}))
+        return
     if args.only == "other":
         print(json.dumps({"only": "other", **time_other_configs(osm, workloads, torch, dev, args.steps, args.warmup)}))
         return
