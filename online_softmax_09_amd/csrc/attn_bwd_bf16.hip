@@ -44,14 +44,14 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdRows = 32 * kBwdWaves;    // query rows (dQ) or keys (dK/dV) per block
 constexpr int kT = 64;                      // rows per streamed tile
-constexpr int kBwdRound = 16 * kBwdThreads; // bytes one block-wide 16-byte copy moves
+constexpr int kDkdvWaves = 8;               // dK/dV: two roles x four key groups
+constexpr int kDkdvThreads = 64 * kDkdvWaves;
 
 template <int D>
 struct BLayout {
     static constexpr int RB = 2 * D;               // bytes per row
     static constexpr int NCH = RB / 16;            // 16-byte chunks per row
     static constexpr int TILE = kT * RB;           // bytes per tile
-    static constexpr int ROUNDS = TILE / kBwdRound;
     // Chunk position of logical chunk c in row r is c ^ swz(r).  d = 128 (a row spans
     // all 64 banks): the low two bits of the row pick bits 2..3 of the permutation and
     // bits 2..3 of the row pick bits 0..1, so 16 consecutive rows see 16 different
@@ -81,22 +81,24 @@ struct BwdParams {
 };
 
 // One 64-row tile of a [N, D] bf16 slab (rows r0 .. r0 + 63 of `head`) from HBM
-// straight to LDS, by all kBwdThreads threads of the block; `src_off` is the thread's
+// straight to LDS, by all THREADS threads of the block; `src_off` is the thread's
 // fixed source offset within a round (see the kernels).  Rows at or past N read as
 // zeros; live = false fills the tile with zeros without reading memory.
-template <int D>
+template <int D, int THREADS = kBwdThreads>
 __device__ __forceinline__ void tile_to_lds(char* lds, const uint16_t* head, int r0, int N, int wave,
                                             int src_off, bool live) {
     using L = BLayout<D>;
+    constexpr int kRound = 16 * THREADS;  // bytes one block-wide 16-byte copy moves
+    constexpr int kRounds = L::TILE / kRound;
     const int rows = live ? min(N - r0, kT) : 0;
     const char* base = reinterpret_cast<const char*>(head) + (live ? (int64_t)r0 * L::RB : 0);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, rows * L::RB, kBufferWord3);
     char* dst = lds + 1024 * wave;  // the wave's 1 KiB of each round; lane offset implicit
 #pragma unroll
-    for (int r = 0; r < L::ROUNDS; ++r)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + kBwdRound * r), 16, src_off,
-                                                 kBwdRound * r, 0, 0);
+    for (int r = 0; r < kRounds; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + kRound * r), 16, src_off, kRound * r, 0,
+                                                 0);
 }
 
 // 64 floats (rows r0 .. r0 + 63 of a per-row vector) to LDS by one wavefront; rows at
@@ -109,26 +111,27 @@ __device__ __forceinline__ void rowvec_to_lds(float* lds, const float* vec, int 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, 4 * lane, 0, 0, 0);
 }
 
-// Per-lane LDS offsets for the two access patterns on a BLayout<D> tile.
+// Per-lane LDS offsets for the two access patterns on a BLayout<D> tile.  The swizzle
+// permutes chunk bits that the k-step (bits 1.. of the chunk index) and the output
+// block (bits 2.. of it) occupy, and never carries, so every offset is the k-step 0 or
+// block 0 offset with those bits flipped: one register per pattern.
 template <int D>
 struct TileReads {
     using L = BLayout<D>;
-    static constexpr int KS = D / 16;
-    static constexpr int DB = D / 32;
-    int row[KS];    // 16-byte read of row l32 (+32 sb), logical chunk 2 ks + h
-    int tr_lo[DB];  // transposing read for output columns 32 b .. 32 b + 31, rows 4h + (lane%16)/4
-    int tr_hi[DB];  // the same 8 rows further down
+    int row0;    // 16-byte read of row l32 (+32 sb), logical chunk h; chunk 2 ks + h at row0 ^ 32 ks
+    int tr_lo0;  // transposing read for output columns 0 .. 31, rows 4h + (lane%16)/4;
+                 // columns 32 b .. at tr_lo0 ^ 64 b
+    int tr_hi0;  // the same 8 rows further down
+    __device__ int row(int ks) const { return row0 ^ (32 * ks); }
+    __device__ int tr_lo(int b) const { return tr_lo0 ^ (64 * b); }
+    __device__ int tr_hi(int b) const { return tr_hi0 ^ (64 * b); }
     __device__ void init(int lane) {
         const int l32 = lane & 31, h = lane >> 5;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) row[ks] = l32 * L::RB + 16 * ((2 * ks + h) ^ L::swz(l32));
+        row0 = l32 * L::RB + 16 * (h ^ L::swz(l32));
         const int vr = 4 * h + ((lane & 15) >> 2);
-#pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            const int col = 64 * b + 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
-            tr_lo[b] = vr * L::RB + 16 * ((col >> 4) ^ L::swz(vr)) + (col & 15);
-            tr_hi[b] = (vr + 8) * L::RB + 16 * ((col >> 4) ^ L::swz(vr + 8)) + (col & 15);
-        }
+        const int col = 32 * ((lane >> 4) & 1) + 8 * (lane & 3);
+        tr_lo0 = vr * L::RB + 16 * ((col >> 4) ^ L::swz(vr)) + (col & 15);
+        tr_hi0 = (vr + 8) * L::RB + 16 * ((col >> 4) ^ L::swz(vr + 8)) + (col & 15);
     }
 };
 
@@ -141,7 +144,7 @@ __device__ __forceinline__ f32x16 rows_times_frag(const char* tile, int sb, cons
     f32x16 a = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 t = *reinterpret_cast<const bf16x8*>(tile + 32 * sb * BLayout<D>::RB + rd.row[ks]);
+        const bf16x8 t = *reinterpret_cast<const bf16x8*>(tile + 32 * sb * BLayout<D>::RB + rd.row(ks));
         a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t, frag[ks], a, 0, 0, 0);
     }
     return a;
@@ -155,7 +158,7 @@ __device__ __forceinline__ void trans_times_packed(f32x16 (&acc)[D / 32], const 
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) {
         const char* base = tile + 16 * g * BLayout<D>::RB;
-        const bf16x8 a = lds_read_tr_pair(base + rd.tr_lo[b], base + rd.tr_hi[b]);
+        const bf16x8 a = lds_read_tr_pair(base + rd.tr_lo(b), base + rd.tr_hi(b));
         acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[b], 0, 0, 0);
     }
 }
@@ -315,15 +318,26 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
 }
 
 // ---------------------------------------------------------------------------------
-// 3. dK and dV.  Lane: key kc = k0 + 32 wave + l32; S / dP rows are queries.
+// 3. dK and dV.  8 wavefronts, 128 keys: key group kg = wave % 4 owns keys
+//    k0 + 32 kg + l32 (one key per lane), in two roles that share a SIMD (waves w and
+//    w + 4).  Per 64-row tile of Q, dO, LSE and D:
+//      phase 1  role A (w < 4):  S = Q K^T, P = exp2(c S - LSE)  -> P to LDS (fp32)
+//               role B (w >= 4): dP = dO V^T
+//      phase 2  role A:  dV^T += dO^T P
+//               role B:  dS = P (dP - D) with A's P from LDS;  dK^T += Q^T dS
+//    Each role issues 32 matrix instructions per tile, and on each SIMD one wavefront's
+//    vector work (A's exponentials in phase 1, B's dS in phase 2) runs beside the other
+//    wavefront's matrix products.  Role A runs at raised issue priority so that its
+//    products, whose results the phase's vector work waits for, go first.
 // ---------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     using L = BLayout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     __shared__ __attribute__((aligned(1024))) char q_lds[2][L::TILE];
     __shared__ __attribute__((aligned(1024))) char do_lds[2][L::TILE];
+    __shared__ __attribute__((aligned(16))) f32x4 p_xch[4][2][4][64];  // [kg][sb][g][lane]
     __shared__ __attribute__((aligned(16))) float lse_lds[2][kT];
     __shared__ __attribute__((aligned(16))) float dl_lds[2][kT];
 
@@ -332,10 +346,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     const int N = p.N;
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3;
+    const bool role_a = wave < 4;
     const int64_t head = (int64_t)bh * N * D;
     const int64_t rowbase = (int64_t)bh * N;
     const int k0 = kt * kBwdRows;
-    const int kw0 = k0 + 32 * wave;
+    const int kw0 = k0 + 32 * kg;
     const int my_k = kw0 + l32;
     const int k_row = min(my_k, N - 1);
 
@@ -344,13 +360,13 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     TileReads<D> rd;
     rd.init(lane);
 
-    bf16x8 kf[KS], vf[KS];
-    load_frag<D>(kf, p.k + head, k_row, h);
-    load_frag<D>(vf, p.v + head, k_row, h);
+    // role A: K fragments (B operand of S = Q K^T); role B: V fragments (dP = dO V^T)
+    bf16x8 frag[KS];
+    load_frag<D>(frag, (role_a ? p.k : p.v) + head, k_row, h);
 
-    f32x16 dk[DB], dv[DB];
+    f32x16 acc[DB];  // role A: dV^T, role B: dK^T (unscaled)
 #pragma unroll
-    for (int b = 0; b < DB; ++b) dk[b] = dv[b] = f32x16{};
+    for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
 
     // query tiles: causal blocks start at the tile holding their first key
     const int i_begin = CAUSAL ? k0 / kT : 0;
@@ -358,8 +374,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     const bool wave_live = kw0 < N;
 
     auto copy_tile = [&](int buf, int i, bool live) {
-        tile_to_lds<D>(q_lds[buf], p.q + head, i * kT, N, wave, src_off, live);
-        tile_to_lds<D>(do_lds[buf], p.dout + head, i * kT, N, wave, src_off, live);
+        tile_to_lds<D, kDkdvThreads>(q_lds[buf], p.q + head, i * kT, N, wave, src_off, live);
+        tile_to_lds<D, kDkdvThreads>(do_lds[buf], p.dout + head, i * kT, N, wave, src_off, live);
         if (wave == 0) rowvec_to_lds(lse_lds[buf], p.lse2 + rowbase, i * kT, N, lane, live);
         if (wave == 1) rowvec_to_lds(dl_lds[buf], p.delta + rowbase, i * kT, N, lane, live);
     };
@@ -367,71 +383,103 @@ __global__ __launch_bounds__(kBwdThreads, 1) void attn_bwd_dkdv_kernel(BwdParams
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 
-    for (int i = i_begin; i < n_q; ++i) {
-        const int cur = (i - i_begin) & 1;
-        copy_tile(cur ^ 1, i + 1, i + 1 < n_q);
-        const char* qt = q_lds[cur];
-        const char* dt = do_lds[cur];
-        const int i0 = i * kT;
-        // P and dS of sub-block sb (rows 32 sb .. 32 sb + 31 of the tile), in place in s, dp
-        auto elementwise = [&](f32x16& s, f32x16& dp, int sb, bool masked) {
-            const int qs0 = i0 + 32 * sb;
+    // The two roles run separate copies of the tile loop (same trip count, same two
+    // barriers per tile), so that neither role's registers are live in the other's.
+    auto tile_loop = [&](auto role) {
+        constexpr bool A = decltype(role)::value;
+        for (int i = i_begin; i < n_q; ++i) {
+            const int cur = (i - i_begin) & 1;
+            copy_tile(cur ^ 1, i + 1, i + 1 < n_q);
+            const char* qt = q_lds[cur];
+            const char* dt = do_lds[cur];
+            const int i0 = i * kT;
+            // sub-block sb = tile rows 32 sb .. 32 sb + 31: skipped when every query
+            // precedes this key group (causal) or lies past N; masked when some entries
+            // are hidden
+            auto live_sb = [&](int sb) {
+                const int qs0 = i0 + 32 * sb;
+                return wave_live && !(CAUSAL && qs0 + 31 < kw0) && qs0 < N;
+            };
+            auto masked_sb = [&](int sb) {
+                const int qs0 = i0 + 32 * sb;
+                return (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
+            };
+            f32x16 x[2];  // role A: S then P; role B: dP then dS
+            if (A) {
+                bf16x8 pk[2][2];
+                // phase 1: S, P (to LDS for role B, packed for dV)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE and D vectors
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_lds[cur][32 * sb + 8 * g + 4 * h]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_lds[cur][32 * sb + 8 * g + 4 * h]);
+                for (int sb = 0; sb < 2; ++sb)
+                    if (live_sb(sb)) x[sb] = rows_times_frag<D>(qt, sb, rd, frag);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int r = 4 * g + u;
-                    float pr = fast_exp2(fmaf(s[r], p.c, -l4[u]));
-                    if (masked) {
-                        const int qq = qs0 + 8 * g + 4 * h + u;
-                        pr = (qq < N && (!CAUSAL || qq >= my_k)) ? pr : 0.0f;
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (!live_sb(sb)) continue;
+                    const bool masked = masked_sb(sb);
+                    const int qs0 = i0 + 32 * sb;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE vector
+                        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_lds[cur][32 * sb + 8 * g + 4 * h]);
+                        f32x4 pv;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int r = 4 * g + u;
+                            float pr = fast_exp2(fmaf(x[sb][r], p.c, -l4[u]));
+                            if (masked) {
+                                const int qq = qs0 + 8 * g + 4 * h + u;
+                                pr = (qq < N && (!CAUSAL || qq >= my_k)) ? pr : 0.0f;
+                            }
+                            x[sb][r] = pr;
+                            pv[u] = pr;
+                        }
+                        p_xch[kg][sb][g][lane] = pv;
                     }
-                    s[r] = pr;
-                    dp[r] = pr * (dp[r] - d4[u]);  // dS
+                    pk[sb][0] = pack8(x[sb], 0);
+                    pk[sb][1] = pack8(x[sb], 1);
+                }
+                __syncthreads();
+                // phase 2: dV^T += dO^T P
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (!live_sb(sb)) continue;
+                    trans_times_packed<D>(acc, dt, 2 * sb + 0, rd, pk[sb][0]);
+                    trans_times_packed<D>(acc, dt, 2 * sb + 1, rd, pk[sb][1]);
+                }
+            } else {
+                // phase 1: dP
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+                    if (live_sb(sb)) x[sb] = rows_times_frag<D>(dt, sb, rd, frag);
+                __syncthreads();
+                // phase 2: dS = P (dP - D), dK^T += Q^T dS
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (!live_sb(sb)) continue;
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_lds[cur][32 * sb + 8 * g + 4 * h]);
+                        const f32x4 pv = p_xch[kg][sb][g][lane];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) x[sb][4 * g + u] = pv[u] * (x[sb][4 * g + u] - d4[u]);
+                    }
+                    trans_times_packed<D>(acc, qt, 2 * sb + 0, rd, pack8(x[sb], 0));
+                    trans_times_packed<D>(acc, qt, 2 * sb + 1, rd, pack8(x[sb], 1));
                 }
             }
-        };
-        auto accumulate = [&](const f32x16& s, const f32x16& dp, int sb) {
-            trans_times_packed<D>(dv, dt, 2 * sb + 0, rd, pack8(s, 0));
-            trans_times_packed<D>(dv, dt, 2 * sb + 1, rd, pack8(s, 1));
-            trans_times_packed<D>(dk, qt, 2 * sb + 0, rd, pack8(dp, 0));
-            trans_times_packed<D>(dk, qt, 2 * sb + 1, rd, pack8(dp, 1));
-        };
-        // Both sub-blocks whole and unmasked: all four score products first, so that the
-        // compiler can run each sub-block's vector work beside the other's matrix
-        // products (explicit interleaving with sched_group_barrier measured slower).
-        const bool full = wave_live && i0 + kT <= N && (!CAUSAL || i0 >= kw0 + 31);
-        if (full) {
-            f32x16 s0 = rows_times_frag<D>(qt, 0, rd, kf);
-            f32x16 dp0 = rows_times_frag<D>(dt, 0, rd, vf);
-            f32x16 s1 = rows_times_frag<D>(qt, 1, rd, kf);
-            f32x16 dp1 = rows_times_frag<D>(dt, 1, rd, vf);
-            elementwise(s0, dp0, 0, false);
-            accumulate(s0, dp0, 0);
-            elementwise(s1, dp1, 1, false);
-            accumulate(s1, dp1, 1);
-        } else {
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                const int qs0 = i0 + 32 * sb;  // first query of the sub-block
-                // causal: skip sub-blocks whose queries all precede this wave's keys
-                if (!wave_live || (CAUSAL && qs0 + 31 < kw0) || qs0 >= N) continue;
-                const bool masked = (CAUSAL && qs0 < kw0 + 31) || (qs0 + 32 > N);
-                f32x16 s = rows_times_frag<D>(qt, sb, rd, kf);    // S rows = queries
-                f32x16 dp = rows_times_frag<D>(dt, sb, rd, vf);   // dP
-                elementwise(s, dp, sb, masked);
-                accumulate(s, dp, sb);
-            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
+    };
+    if (role_a) {
+        __builtin_amdgcn_s_setprio(1);
+        tile_loop(std::true_type{});
+    } else {
+        tile_loop(std::false_type{});
     }
+    __builtin_amdgcn_s_setprio(0);
     if (wave_live && my_k < N) {
-        store_rows<D>(p.dv + head, my_k, h, dv, 1.0f);
-        store_rows<D>(p.dk + head, my_k, h, dk, p.scale);
+        if (role_a) store_rows<D>(p.dv + head, my_k, h, acc, 1.0f);
+        else store_rows<D>(p.dk + head, my_k, h, acc, p.scale);
     }
 }
 
@@ -440,7 +488,7 @@ hipError_t launch_main(BwdParams p, hipStream_t st) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kBwdThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kBwdThreads), 0, st, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kDkdvThreads), 0, st, p);
     return hipGetLastError();
 }
 
