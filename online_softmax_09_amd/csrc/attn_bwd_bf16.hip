@@ -111,6 +111,15 @@ __device__ __forceinline__ void rowvec_to_lds(float* lds, const float* vec, int 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, 4 * lane, 0, 0, 0);
 }
 
+// Block barrier for LDS data written with ds_write: waits for this wavefront's LDS
+// operations only, not for HBM -> LDS copies still in flight (a workgroup fence would
+// wait for those too, since they write LDS).  The asm statement is also a compiler
+// barrier for memory accesses.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // Per-lane LDS offsets for the two access patterns on a BLayout<D> tile.  The swizzle
 // permutes chunk bits that the k-step (bits 1.. of the chunk index) and the output
 // block (bits 2.. of it) occupy, and never carries, so every offset is the k-step 0 or
@@ -137,11 +146,24 @@ struct TileReads {
 
 // acc (32 rows of the tile from row 32 sb, x 32 columns) = A B: A = 16-byte row reads of
 // `tile` (rows = the accumulator's rows, k = the D columns), B = frag (per lane: column
-// l32, k-slots 8h..8h+7 of each 16-wide k-step).
-template <int D>
+// l32, k-slots 8h..8h+7 of each 16-wide k-step).  AHEAD: all of the sub-block's A
+// operands are read before the first product (kernels with registers to spare), so that
+// the products do not wait on LDS latency one pair at a time.
+template <int D, bool AHEAD = false>
 __device__ __forceinline__ f32x16 rows_times_frag(const char* tile, int sb, const TileReads<D>& rd,
                                                   const bf16x8 (&frag)[D / 16]) {
     f32x16 a = f32x16{};
+    if (AHEAD) {
+        bf16x8 t[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            t[ks] = *reinterpret_cast<const bf16x8*>(tile + 32 * sb * BLayout<D>::RB + rd.row(ks));
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t[ks], frag[ks], a, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);  // every read, then
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);  // every product
+        return a;
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 t = *reinterpret_cast<const bf16x8*>(tile + 32 * sb * BLayout<D>::RB + rd.row(ks));
@@ -152,12 +174,22 @@ __device__ __forceinline__ f32x16 rows_times_frag(const char* tile, int sb, cons
 
 // acc[b] (output columns 32 b.., x 32 lanes' columns) += T^T B over the 16 tile rows
 // of group g: A = transposing reads of `tile`, B = the packed operand for group g.
-template <int D>
+template <int D, bool AHEAD = false>
 __device__ __forceinline__ void trans_times_packed(f32x16 (&acc)[D / 32], const char* tile, int g,
                                                    const TileReads<D>& rd, const bf16x8& bop) {
+    const char* base = tile + 16 * g * BLayout<D>::RB;
+    if (AHEAD) {
+        bf16x8 a[D / 32];
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) a[b] = lds_read_tr_pair(base + rd.tr_lo(b), base + rd.tr_hi(b));
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[b], bop, acc[b], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 0);
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < D / 32; ++b) {
-        const char* base = tile + 16 * g * BLayout<D>::RB;
         const bf16x8 a = lds_read_tr_pair(base + rd.tr_lo(b), base + rd.tr_hi(b));
         acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, acc[b], 0, 0, 0);
     }
@@ -244,8 +276,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
     using L = BLayout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(1024))) char k_lds[2][L::TILE];
-    __shared__ __attribute__((aligned(1024))) char v_lds[2][L::TILE];
+    // Double buffers as separate objects, selected at compile time, so that the compiler
+    // can tell the buffer being filled from the one being read (it would otherwise wait
+    // for the copies in flight before every read).
+    __shared__ __attribute__((aligned(1024))) char k_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[L::TILE];
 
     int bh, qt;
     block_coords(p, CAUSAL, true, bh, qt);
@@ -279,19 +316,20 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
     const bool wave_live = qw0 < N;
     const int n_w = !wave_live ? 0 : CAUSAL ? min(n_kv, min(qw0 + 31, N - 1) / kT + 1) : n_kv;
 
-    tile_to_lds<D>(k_lds[0], p.k + head, 0, N, wave, src_off, true);
-    tile_to_lds<D>(v_lds[0], p.v + head, 0, N, wave, src_off, true);
+    tile_to_lds<D>(k_lds0, p.k + head, 0, N, wave, src_off, true);
+    tile_to_lds<D>(v_lds0, p.v + head, 0, N, wave, src_off, true);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
-    for (int j = 0; j < n_kv; ++j) {
-        const int cur = j & 1;
+    // tile j; PAR = j % 2 at compile time
+    auto tile = [&](auto par, int j) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par)::value;
         // prefetch the next tile into the other buffers (read two barriers ago)
-        tile_to_lds<D>(k_lds[cur ^ 1], p.k + head, (j + 1) * kT, N, wave, src_off, j + 1 < n_kv);
-        tile_to_lds<D>(v_lds[cur ^ 1], p.v + head, (j + 1) * kT, N, wave, src_off, j + 1 < n_kv);
+        tile_to_lds<D>(PAR ? k_lds0 : k_lds1, p.k + head, (j + 1) * kT, N, wave, src_off, j + 1 < n_kv);
+        tile_to_lds<D>(PAR ? v_lds0 : v_lds1, p.v + head, (j + 1) * kT, N, wave, src_off, j + 1 < n_kv);
         if (j < n_w) {
-            const char* kt = k_lds[cur];
-            const char* vt = v_lds[cur];
+            const char* kt = PAR ? k_lds1 : k_lds0;
+            const char* vt = PAR ? v_lds1 : v_lds0;
             const int j0 = j * kT;
             const bool masked = (CAUSAL && j0 + kT - 1 > qw0) || (j0 + kT > N);
 #pragma unroll
@@ -313,7 +351,13 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tiles have landed
         __syncthreads();
+    };
+    int j = 0;
+    for (; j + 1 < n_kv; j += 2) {
+        tile(std::integral_constant<int, 0>{}, j);
+        tile(std::integral_constant<int, 1>{}, j + 1);
     }
+    if (j < n_kv) tile(std::integral_constant<int, 0>{}, j);
     if (wave_live && my_q < N) store_rows<D>(p.dq + head, my_q, h, acc, p.scale);
 }
 
@@ -335,11 +379,16 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
     using L = BLayout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(1024))) char q_lds[2][L::TILE];
-    __shared__ __attribute__((aligned(1024))) char do_lds[2][L::TILE];
+    // Double buffers as separate objects, selected at compile time (see the dQ kernel).
+    __shared__ __attribute__((aligned(1024))) char q_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char q_lds1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char do_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char do_lds1[L::TILE];
     __shared__ __attribute__((aligned(16))) f32x4 p_xch[4][2][4][64];  // [kg][sb][g][lane]
-    __shared__ __attribute__((aligned(16))) float lse_lds[2][kT];
-    __shared__ __attribute__((aligned(16))) float dl_lds[2][kT];
+    __shared__ __attribute__((aligned(16))) float lse_lds0[kT];
+    __shared__ __attribute__((aligned(16))) float lse_lds1[kT];
+    __shared__ __attribute__((aligned(16))) float dl_lds0[kT];
+    __shared__ __attribute__((aligned(16))) float dl_lds1[kT];
 
     int bh, kt;
     block_coords(p, CAUSAL, false, bh, kt);
@@ -373,25 +422,31 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
     const int n_q = (N + kT - 1) / kT;
     const bool wave_live = kw0 < N;
 
-    auto copy_tile = [&](int buf, int i, bool live) {
-        tile_to_lds<D, kDkdvThreads>(q_lds[buf], p.q + head, i * kT, N, wave, src_off, live);
-        tile_to_lds<D, kDkdvThreads>(do_lds[buf], p.dout + head, i * kT, N, wave, src_off, live);
-        if (wave == 0) rowvec_to_lds(lse_lds[buf], p.lse2 + rowbase, i * kT, N, lane, live);
-        if (wave == 1) rowvec_to_lds(dl_lds[buf], p.delta + rowbase, i * kT, N, lane, live);
+    auto copy_tile = [&](auto buf, int i, bool live) __attribute__((always_inline)) {
+        constexpr int BUF = decltype(buf)::value;
+        tile_to_lds<D, kDkdvThreads>(BUF ? q_lds1 : q_lds0, p.q + head, i * kT, N, wave, src_off, live);
+        tile_to_lds<D, kDkdvThreads>(BUF ? do_lds1 : do_lds0, p.dout + head, i * kT, N, wave, src_off, live);
+        if (wave == 0) rowvec_to_lds(BUF ? lse_lds1 : lse_lds0, p.lse2 + rowbase, i * kT, N, lane, live);
+        if (wave == 1) rowvec_to_lds(BUF ? dl_lds1 : dl_lds0, p.delta + rowbase, i * kT, N, lane, live);
     };
-    copy_tile(0, i_begin, i_begin < n_q);
+    copy_tile(std::integral_constant<int, 0>{}, i_begin, i_begin < n_q);
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
 
     // The two roles run separate copies of the tile loop (same trip count, same two
-    // barriers per tile), so that neither role's registers are live in the other's.
-    auto tile_loop = [&](auto role) {
+    // barriers per tile), so that neither role's registers are live in the other's.  The
+    // mid-tile barrier orders only the P exchange in LDS; the next tile's copies, issued at
+    // the start of the tile, have until the end-of-tile barrier to land.
+    // tile i, held in buffer PAR = (i - i_begin) % 2 (compile time)
+    auto tile = [&](auto role, auto par, int i) __attribute__((always_inline)) {
         constexpr bool A = decltype(role)::value;
-        for (int i = i_begin; i < n_q; ++i) {
-            const int cur = (i - i_begin) & 1;
-            copy_tile(cur ^ 1, i + 1, i + 1 < n_q);
-            const char* qt = q_lds[cur];
-            const char* dt = do_lds[cur];
+        constexpr int PAR = decltype(par)::value;
+        {
+            copy_tile(std::integral_constant<int, PAR ^ 1>{}, i + 1, i + 1 < n_q);
+            const char* qt = PAR ? q_lds1 : q_lds0;
+            const char* dt = PAR ? do_lds1 : do_lds0;
+            const float* lse_t = PAR ? lse_lds1 : lse_lds0;
+            const float* dl_t = PAR ? dl_lds1 : dl_lds0;
             const int i0 = i * kT;
             // sub-block sb = tile rows 32 sb .. 32 sb + 31: skipped when every query
             // precedes this key group (causal) or lies past N; masked when some entries
@@ -410,22 +465,23 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
                 // phase 1: S, P (to LDS for role B, packed for dV)
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
-                    if (live_sb(sb)) x[sb] = rows_times_frag<D>(qt, sb, rd, frag);
-#pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    if (!live_sb(sb)) continue;
-                    const bool masked = masked_sb(sb);
+                    if (live_sb(sb)) x[sb] = rows_times_frag<D, true>(qt, sb, rd, frag);
+                // P of sub-block sb; the mask is a compile-time choice so that whole
+                // sub-blocks (the common case) run without per-element branches
+                auto probs = [&](auto masked_c, int sb) __attribute__((always_inline)) {
+                    constexpr bool MASKED = decltype(masked_c)::value;
                     const int qs0 = i0 + 32 * sb;
+                    f32x4 l4[4];  // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE vector
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4*>(&lse_t[32 * sb + 8 * g + 4 * h]);
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE vector
-                        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_lds[cur][32 * sb + 8 * g + 4 * h]);
                         f32x4 pv;
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             const int r = 4 * g + u;
-                            float pr = fast_exp2(fmaf(x[sb][r], p.c, -l4[u]));
-                            if (masked) {
+                            float pr = fast_exp2(fmaf(x[sb][r], p.c, -l4[g][u]));
+                            if (MASKED) {
                                 const int qq = qs0 + 8 * g + 4 * h + u;
                                 pr = (qq < N && (!CAUSAL || qq >= my_k)) ? pr : 0.0f;
                             }
@@ -436,39 +492,56 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
                     }
                     pk[sb][0] = pack8(x[sb], 0);
                     pk[sb][1] = pack8(x[sb], 1);
+                };
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (!live_sb(sb)) continue;
+                    if (masked_sb(sb)) probs(std::true_type{}, sb);
+                    else probs(std::false_type{}, sb);
                 }
-                __syncthreads();
+                lds_barrier();  // P is in LDS; the next tile's copies stay in flight
                 // phase 2: dV^T += dO^T P
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
                     if (!live_sb(sb)) continue;
-                    trans_times_packed<D>(acc, dt, 2 * sb + 0, rd, pk[sb][0]);
-                    trans_times_packed<D>(acc, dt, 2 * sb + 1, rd, pk[sb][1]);
+                    trans_times_packed<D, true>(acc, dt, 2 * sb + 0, rd, pk[sb][0]);
+                    trans_times_packed<D, true>(acc, dt, 2 * sb + 1, rd, pk[sb][1]);
                 }
             } else {
                 // phase 1: dP
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
-                    if (live_sb(sb)) x[sb] = rows_times_frag<D>(dt, sb, rd, frag);
-                __syncthreads();
+                    if (live_sb(sb)) x[sb] = rows_times_frag<D, true>(dt, sb, rd, frag);
+                lds_barrier();
                 // phase 2: dS = P (dP - D), dK^T += Q^T dS
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
                     if (!live_sb(sb)) continue;
+                    f32x4 d4[4], pv[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dl_lds[cur][32 * sb + 8 * g + 4 * h]);
-                        const f32x4 pv = p_xch[kg][sb][g][lane];
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) x[sb][4 * g + u] = pv[u] * (x[sb][4 * g + u] - d4[u]);
+                        d4[g] = *reinterpret_cast<const f32x4*>(&dl_t[32 * sb + 8 * g + 4 * h]);
+                        pv[g] = p_xch[kg][sb][g][lane];
                     }
-                    trans_times_packed<D>(acc, qt, 2 * sb + 0, rd, pack8(x[sb], 0));
-                    trans_times_packed<D>(acc, qt, 2 * sb + 1, rd, pack8(x[sb], 1));
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) x[sb][4 * g + u] = pv[g][u] * (x[sb][4 * g + u] - d4[g][u]);
+                    trans_times_packed<D, true>(acc, qt, 2 * sb + 0, rd, pack8(x[sb], 0));
+                    trans_times_packed<D, true>(acc, qt, 2 * sb + 1, rd, pack8(x[sb], 1));
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed
             __syncthreads();
         }
+    };
+    auto tile_loop = [&](auto role) __attribute__((always_inline)) {
+        int i = i_begin;
+        for (; i + 1 < n_q; i += 2) {
+            tile(role, std::integral_constant<int, 0>{}, i);
+            tile(role, std::integral_constant<int, 1>{}, i + 1);
+        }
+        if (i < n_q) tile(role, std::integral_constant<int, 0>{}, i);
     };
     if (role_a) {
         __builtin_amdgcn_s_setprio(1);
