@@ -331,23 +331,32 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
             const char* kt = PAR ? k_lds1 : k_lds0;
             const char* vt = PAR ? v_lds1 : v_lds0;
             const int j0 = j * kT;
-            const bool masked = (CAUSAL && j0 + kT - 1 > qw0) || (j0 + kT > N);
+            // the mask is a compile-time choice so that whole tiles (the common case) run
+            // without per-element branches
+            auto body = [&](auto masked_c) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked_c)::value;
+                // key j0 + 32 sb + 8 (r / 4) + 4 h + r % 4 is visible when its offset from
+                // j0 + 4 h is at most lim (a compile-time offset against one register)
+                const int lim = key_lim - j0 - 4 * h;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                f32x16 s = rows_times_frag<D>(kt, sb, rd, qf);    // S^T rows = keys
-                f32x16 dp = rows_times_frag<D>(vt, sb, rd, dof);  // dP^T
+                for (int sb = 0; sb < 2; ++sb) {
+                    f32x16 s = rows_times_frag<D>(kt, sb, rd, qf);    // S^T rows = keys
+                    f32x16 dp = rows_times_frag<D>(vt, sb, rd, dof);  // dP^T
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float pr = fast_exp2(fmaf(s[r], p.c, -lse2));
-                    if (masked) {
-                        const int key = j0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        pr = key <= key_lim ? pr : 0.0f;
+                    for (int r = 0; r < 16; ++r) {
+                        float pr = fast_exp2(fmaf(s[r], p.c, -lse2));
+                        if (MASKED) pr = 32 * sb + 8 * (r >> 2) + (r & 3) <= lim ? pr : 0.0f;
+                        s[r] = pr * (dp[r] - dlt);  // dS^T
                     }
-                    s[r] = pr * (dp[r] - dlt);  // dS^T
+                    trans_times_packed<D>(acc, kt, 2 * sb + 0, rd, pack8(s, 0));
+                    trans_times_packed<D>(acc, kt, 2 * sb + 1, rd, pack8(s, 1));
+                    // keep the two sub-blocks apart: overlapping them raises the register
+                    // count past what two wavefronts per SIMD allow
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                trans_times_packed<D>(acc, kt, 2 * sb + 0, rd, pack8(s, 0));
-                trans_times_packed<D>(acc, kt, 2 * sb + 1, rd, pack8(s, 1));
-            }
+            };
+            if ((CAUSAL && j0 + kT - 1 > qw0) || (j0 + kT > N)) body(std::true_type{});
+            else body(std::false_type{});
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tiles have landed
         __syncthreads();
@@ -470,7 +479,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
                 // sub-blocks (the common case) run without per-element branches
                 auto probs = [&](auto masked_c, int sb) __attribute__((always_inline)) {
                     constexpr bool MASKED = decltype(masked_c)::value;
-                    const int qs0 = i0 + 32 * sb;
+                    // query qs0 + 8 g + 4 h + u is visible when its offset o = 8 g + u from
+                    // qs0 + 4 h satisfies o < n_lim and (causal) o >= k_lim
+                    const int qb = i0 + 32 * sb + 4 * h;
+                    const int n_lim = N - qb, k_lim = my_k - qb;
                     f32x4 l4[4];  // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE vector
 #pragma unroll
                     for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4*>(&lse_t[32 * sb + 8 * g + 4 * h]);
@@ -482,8 +494,8 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
                             const int r = 4 * g + u;
                             float pr = fast_exp2(fmaf(x[sb][r], p.c, -l4[g][u]));
                             if (MASKED) {
-                                const int qq = qs0 + 8 * g + 4 * h + u;
-                                pr = (qq < N && (!CAUSAL || qq >= my_k)) ? pr : 0.0f;
+                                const int o = 8 * g + u;
+                                pr = (o < n_lim && (!CAUSAL || o >= k_lim)) ? pr : 0.0f;
                             }
                             x[sb][r] = pr;
                             pv[u] = pr;
