@@ -375,13 +375,14 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
 //    k0 + 32 kg + l32 (one key per lane), in two roles that share a SIMD (waves w and
 //    w + 4).  Per 64-row tile of Q, dO, LSE and D:
 //      phase 1  role A (w < 4):  S = Q K^T, P = exp2(c S - LSE)  -> P to LDS (fp32)
-//               role B (w >= 4): dP = dO V^T
-//      phase 2  role A:  dV^T += dO^T P
+//               role B (w >= 4): dP = dO V^T, then dP - D
+//      phase 2  role A:  P packed to bf16, dV^T += dO^T P
 //               role B:  dS = P (dP - D) with A's P from LDS;  dK^T += Q^T dS
 //    Each role issues 32 matrix instructions per tile, and on each SIMD one wavefront's
-//    vector work (A's exponentials in phase 1, B's dS in phase 2) runs beside the other
-//    wavefront's matrix products.  Role A runs at raised issue priority so that its
-//    products, whose results the phase's vector work waits for, go first.
+//    vector work (mostly A's exponentials in phase 1, B's dS in phase 2) runs beside the
+//    other wavefront's matrix products; the vector steps that need no exchange sit in the
+//    phase where their role has time to spare.  Role A runs at raised issue priority so
+//    that its products, whose results the phase's vector work waits for, go first.
 // ---------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
@@ -470,7 +471,6 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
             };
             f32x16 x[2];  // role A: S then P; role B: dP then dS
             if (A) {
-                bf16x8 pk[2][2];
                 // phase 1: S, P (to LDS for role B, packed for dV)
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb)
@@ -502,8 +502,6 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
                         }
                         p_xch[kg][sb][g][lane] = pv;
                     }
-                    pk[sb][0] = pack8(x[sb], 0);
-                    pk[sb][1] = pack8(x[sb], 1);
                 };
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
@@ -512,33 +510,39 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
                     else probs(std::false_type{}, sb);
                 }
                 lds_barrier();  // P is in LDS; the next tile's copies stay in flight
-                // phase 2: dV^T += dO^T P
+                // phase 2: dV^T += dO^T P (P packed here, where role A has time to spare)
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
                     if (!live_sb(sb)) continue;
-                    trans_times_packed<D, true>(acc, dt, 2 * sb + 0, rd, pk[sb][0]);
-                    trans_times_packed<D, true>(acc, dt, 2 * sb + 1, rd, pk[sb][1]);
+                    trans_times_packed<D, true>(acc, dt, 2 * sb + 0, rd, pack8(x[sb], 0));
+                    trans_times_packed<D, true>(acc, dt, 2 * sb + 1, rd, pack8(x[sb], 1));
                 }
             } else {
-                // phase 1: dP
+                // phase 1: dP - D (role B has time to spare here)
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb)
-                    if (live_sb(sb)) x[sb] = rows_times_frag<D, true>(dt, sb, rd, frag);
+                for (int sb = 0; sb < 2; ++sb) {
+                    if (!live_sb(sb)) continue;
+                    x[sb] = rows_times_frag<D, true>(dt, sb, rd, frag);
+                    f32x4 d4[4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const f32x4*>(&dl_t[32 * sb + 8 * g + 4 * h]);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) x[sb][4 * g + u] -= d4[g][u];
+                }
                 lds_barrier();
                 // phase 2: dS = P (dP - D), dK^T += Q^T dS
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
                     if (!live_sb(sb)) continue;
-                    f32x4 d4[4], pv[4];
+                    f32x4 pv[4];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        d4[g] = *reinterpret_cast<const f32x4*>(&dl_t[32 * sb + 8 * g + 4 * h]);
-                        pv[g] = p_xch[kg][sb][g][lane];
-                    }
+                    for (int g = 0; g < 4; ++g) pv[g] = p_xch[kg][sb][g][lane];
 #pragma unroll
                     for (int g = 0; g < 4; ++g)
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) x[sb][4 * g + u] = pv[g][u] * (x[sb][4 * g + u] - d4[g][u]);
+                        for (int u = 0; u < 4; ++u) x[sb][4 * g + u] *= pv[g][u];  // dS = P (dP - D)
                     trans_times_packed<D, true>(acc, qt, 2 * sb + 0, rd, pack8(x[sb], 0));
                     trans_times_packed<D, true>(acc, qt, 2 * sb + 1, rd, pack8(x[sb], 1));
                 }
