@@ -18,11 +18,13 @@
 //      dP^T = V dO^T put one query row in each lane (Q and dO fragments stay in
 //      registers), dS^T is formed in place and packed to bf16, and
 //      dQ^T += K^T dS^T reads K^T with the transposing LDS load.
-//   3. dK/dV: one block per 128 keys, 4 wavefronts of 32 keys, streaming 64-row tiles
-//      of Q, dO, LSE and D through LDS.  Here S = Q K^T and dP = dO V^T put one key in
-//      each lane (K and V fragments stay in registers); P and dS, packed to bf16 as
-//      they lie, are the B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A
-//      operands are transposing reads of the dO and Q tiles.
+//   3. dK/dV: one block per 128 keys, 8 wavefronts (4 groups of 32 keys, two roles per
+//      group), streaming 64-row tiles of Q, dO, LSE and D through LDS.  Here S = Q K^T
+//      and dP = dO V^T put one key in each lane (K or V fragments stay in registers);
+//      P and dS, packed to bf16 as they lie, are the B operands of dV^T += dO^T P and
+//      dK^T += Q^T dS, whose A operands are transposing reads of the dO and Q tiles.
+//      One role computes S, P and dV, the other dP, dS and dK, with P passed through
+//      LDS (see the kernel).
 // Computing dQ in its own pass (recomputing S and dP there) keeps every gradient
 // element owned by one lane of one block: no atomics, and results are bitwise
 // repeatable.
@@ -350,9 +352,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
                     }
                     trans_times_packed<D>(acc, kt, 2 * sb + 0, rd, pack8(s, 0));
                     trans_times_packed<D>(acc, kt, 2 * sb + 1, rd, pack8(s, 1));
-                    // keep the two sub-blocks apart: overlapping them raises the register
-                    // count past what two wavefronts per SIMD allow
-                    __builtin_amdgcn_sched_barrier(0);
                 }
             };
             if ((CAUSAL && j0 + kT - 1 > qw0) || (j0 + kT > N)) body(std::true_type{});

@@ -140,8 +140,8 @@ __global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y
 // (section 4's update, a chunk at a time); scan 2 re-reads and writes.
 // ---------------------------------------------------------------------------
 template <bool VEC4>
-__global__ __launch_bounds__(256) void softmax_rows_stream(const float* x, float* y, int64_t rows,
-                                                           int64_t cols) {
+__global__ __launch_bounds__(256) void softmax_rows_stream(const float* x, float* y,
+                                                           int64_t /* rows: one block each */, int64_t cols) {
     using U = typename Unit<VEC4>::T;
     constexpr int CH = 4;  // units per thread per step, loaded together
     const int64_t row = blockIdx.x;
