@@ -139,6 +139,7 @@ struct Wave {
     float c;         // |scale| log2(e)
     float base;      // finite stand-in for m while a tile is exponentiated
     float alpha;     // exp2(m_old - m_new) of the tile in flight
+    float psum[4];   // partial row sums of the tile in flight (split softmax, d = 64)
     int half, key_lim;
 
     // S^T = K Q^T for the two 32-key halves of a tile (A = K rows from LDS).
@@ -180,6 +181,8 @@ struct Wave {
         base = safe_base(m_new);
         alpha = fast_exp2(m - base);  // 1 when m stays; 0 when m = -inf
         m = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) psum[i] = 0.0f;
     }
 
     template <bool MASK>
@@ -206,6 +209,29 @@ struct Wave {
                 pf[2 * sb + hb] = __builtin_bit_cast(v8, w);
             }
     }
+
+    // The same work split in two for d = 64 (see the kernel): the exponentials of one
+    // 32-key half, summed into psum and packed straight into the P^T fragments (the
+    // previous tile's fragments must have been consumed), then the update of l.  The
+    // arithmetic and its order are those of expsum.
+    template <bool MASK, int SB>
+    __device__ __forceinline__ void exp_half(f32x16 (&st)[2], int j0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float e = fast_exp2(fmaf(st[SB][r], c, -base));
+            if (MASK) e = visible(j0, SB, r) ? e : 0.0f;
+            st[SB][r] = e;
+            psum[r & 3] += e;
+        }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            u32x4 w;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) w[t] = E::pack2(st[SB][8 * hb + 2 * t], st[SB][8 * hb + 2 * t + 1]);
+            pf[2 * SB + hb] = __builtin_bit_cast(v8, w);
+        }
+    }
+    __device__ __forceinline__ void finish() { l = alpha * l + ((psum[0] + psum[1]) + (psum[2] + psum[3])); }
 
     // O^T *= alpha, skipped (per wavefront) when no row moved its reference maximum.
     __device__ __forceinline__ void rescale() {
@@ -342,47 +368,75 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     auto is_masked = [&](int j) { return (CAUSAL && j * kBN + kBN - 1 > qw0) || (j * kBN + kBN > N); };
     // GEMM_j (plus, for group 0, the copy of K_{j+2}).  PAR = j % 2 at compile time,
     // so every buffer access names one LDS object.
-    auto gemm = [&](auto par, int j, f32x16(&sn)[2], bool copy_k) {
+    // d = 64 halves the matrix work of a tile but not its vector work, so there the
+    // matrix half-step also takes the row maximum of S_j and the exponentials of its
+    // first 32 keys (SPLIT), between its own matrix instructions; the softmax half-step
+    // keeps the other 32 keys.  At d = 128 the two halves are already even and moving
+    // work measured slower.
+    constexpr bool SPLIT = D == 64;
+    auto gemm = [&](auto par, int j, f32x16(&sc)[2], f32x16(&sn)[2], bool copy_k) {
         constexpr int PAR = decltype(par)::value;
         const char* vprev = PAR ? v_lds0 : v_lds1;  // holds V_{j-1}
         const char* knext = PAR ? k_lds0 : k_lds1;  // holds K_{j+1}
         const bool do_pv = j >= 1 && j - 1 < n_w;
         const bool do_qk = j + 1 < n_w;
+        const bool do_sm = SPLIT && j < n_w;
+        const int j0 = j * kBN;
         __builtin_amdgcn_s_setprio(1);
-        if (do_pv && do_qk) {
+        if (do_pv && do_qk && !(SPLIT && is_masked(j))) {
             if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gwave, k_src);
             w.pv(vprev);
+            if constexpr (SPLIT) w.template prep<false>(sc, j0);
             w.qk(sn, knext);
+            if constexpr (SPLIT) w.template exp_half<false, 0>(sc, j0);
             // Keep LDS operand reads a few matrix instructions ahead of their use and
-            // spread the copies between the matrix instructions.
+            // spread the copies (and, with SPLIT, the vector work) between the matrix
+            // instructions.
             __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (SPLIT) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
                 if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 if (i < 10) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (SPLIT) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
                 if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
         } else {
             if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gwave, k_src);
             if (do_pv) w.pv(vprev);
+            if (do_sm) {
+                if (is_masked(j)) {
+                    w.template prep<true>(sc, j0);
+                    w.template exp_half<true, 0>(sc, j0);
+                } else {
+                    w.template prep<false>(sc, j0);
+                    w.template exp_half<false, 0>(sc, j0);
+                }
+            }
             if (do_qk) w.qk(sn, knext);
         }
         __builtin_amdgcn_s_setprio(0);
     };
     auto softmax = [&](int j, f32x16(&sc)[2]) {
         if (j < 0 || j >= n_w) return;
-        if (is_masked(j)) {
-            w.template prep<true>(sc, j * kBN);
-            w.template expsum<true>(sc, j * kBN);
+        if constexpr (SPLIT) {
+            if (is_masked(j)) w.template exp_half<true, 1>(sc, j * kBN);
+            else w.template exp_half<false, 1>(sc, j * kBN);
+            w.finish();
         } else {
-            w.template prep<false>(sc, j * kBN);
-            w.template expsum<false>(sc, j * kBN);
+            if (is_masked(j)) {
+                w.template prep<true>(sc, j * kBN);
+                w.template expsum<true>(sc, j * kBN);
+            } else {
+                w.template prep<false>(sc, j * kBN);
+                w.template expsum<false>(sc, j * kBN);
+            }
         }
         w.rescale();  // O (holding tiles up to j-1) *= alpha_j before P_j V_j
     };
@@ -392,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
         constexpr int PAR = decltype(par)::value;
         // half-step 2 j
         if (group == 0) {
-            gemm(par, j, s_oth, j + 2 < n_kv);
+            gemm(par, j, s_cur, s_oth, j + 2 < n_kv);
         } else {
             if (j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
             softmax(j - 1, s_oth);
@@ -402,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
         if (group == 0) {
             softmax(j, s_cur);
         } else {
-            gemm(par, j, s_oth, false);
+            gemm(par, j, s_cur, s_oth, false);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K_{j+2} and V_j have landed
         __syncthreads();
