@@ -59,7 +59,7 @@ extern "C" {
 enum {
     MI355ATTN_OK = 0,
     MI355ATTN_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, bad scale, misaligned or overlapping buffers */
-    MI355ATTN_ERR_UNSUPPORTED = -2, /* head dimension or size this build has no kernel for */
+    MI355ATTN_ERR_UNSUPPORTED = -2, /* head dimension or size the library has no kernel for */
     MI355ATTN_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
 };
 
