@@ -75,9 +75,9 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
         if (u < units) {
             ++nvalid;
             if constexpr (U == 8) {
-                const u32x4 xv = *reinterpret_cast<const u32x4*>(p.x + base + 8 * u);
+                const u32x4 xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.x + base + 8 * u));
                 u32x4 rv = u32x4{0, 0, 0, 0};
-                if (p.res) rv = *reinterpret_cast<const u32x4*>(p.res + base + 8 * u);
+                if (p.res) rv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.res + base + 8 * u));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     h[i][2 * j] = bf16_lo(xv[j]) + bf16_lo(rv[j]);
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
                     u32x4 o;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) o[j] = pack_bf16x2(h[i][2 * j], h[i][2 * j + 1]);
-                    *reinterpret_cast<u32x4*>(p.res_out + base + 8 * u) = o;
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p.res_out + base + 8 * u));
                 }
             } else {
                 const float xr = __uint_as_float((uint32_t)p.x[base + u] << 16);
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
                 const float y1 = fmaf((h[i][2 * j + 1] - mean) * rstd, bf16_hi(gv[j]), bf16_hi(bv[j]));
                 o[j] = pack_bf16x2(y0, y1);
             }
-            *reinterpret_cast<u32x4*>(p.y + base + 8 * u) = o;
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(p.y + base + 8 * u));
         } else {
             const float g = __uint_as_float((uint32_t)p.gamma[u] << 16);
             const float b = LAYER ? __uint_as_float((uint32_t)p.beta[u] << 16) : 0.0f;
