@@ -266,3 +266,29 @@ def test_scale_edge_cases(fn, dtype, tol_o, tol_l, causal, scale):
         widen = max(1.0, abs(scale) * math.sqrt(q.shape[-1]))
         tol_o, tol_l = tol_o * widen, tol_l * widen
     assert eo <= tol_o and el <= tol_l
+
+
+@pytest.mark.parametrize("fn,dtype,tol_o,tol_l", [("fa_fwd", "bf16", TOL_BF16_O, TOL_BF16_LSE),
+                                                   ("fa_fwd_f16", "f16", 5e-3, 1e-3)])
+@pytest.mark.parametrize("f", [2, 8, 64])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_score_jumps(d, causal, f, fn, dtype, tol_o, tol_l):
+    """Keys far above the running maximum arrive late in the key loop: key rows 130,
+    300 and 611 are multiplied by f, 2 f and 4 f (powers of two, exact in both
+    formats), so a row's maximum jumps, in later key tiles, by a few to several hundred
+    powers of two.  Small jumps stay under the kernel's lazy threshold (the reference
+    maximum does not move and the probabilities exceed 1); large ones move it and
+    rescale O by alpha, where exp2 of the jump against the old maximum would overflow
+    float32 by far."""
+    dev = need_gpu()
+    q, k, v = workloads.attention_inputs(1, 2, 700, d, seed=workloads.SEED_BASE + 7300 + d, dtype=dtype)
+    k = k.clone()
+    for row, mult in ((130, f), (300, 2 * f), (611, 4 * f)):
+        k[:, :, row] *= mult
+    say(f"case {fn} score jumps d={d} causal={causal} f={f}")
+    o, lse = _gpu(getattr(osm, fn), q, k, v, workloads.default_scale(d), causal, dev)
+    o_ref, lse_ref = oracle.attention(q, k, v, workloads.default_scale(d), causal)
+    eo, el = _report(fn, o, lse, o_ref, lse_ref, 1e-3)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert eo <= tol_o and el <= tol_l
