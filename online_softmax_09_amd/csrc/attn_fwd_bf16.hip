@@ -84,6 +84,27 @@ struct Layout {
     __device__ static constexpr int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 2 * (r & 3); }
 };
 
+// Causal diagonal tiles.  The last key tile a wavefront needs starts D0 = 0 or 32 rows
+// before the wavefront's first query row (query rows come in 32s, key tiles in 64s), and
+// no earlier tile holds a hidden key.  In the S^T accumulator lane l holds query row
+// l mod 32 and, in element r of half sb, the key 4 (l / 32) + 32 sb + 8 (r / 4) + r mod 4
+// of the tile, so which lanes see that key is a constant bit mask per (D0, sb, r).
+struct DiagMasks {
+    uint64_t m[2][2][16];  // [D0 / 32][sb][r]: bit l set when lane l sees the key
+};
+constexpr DiagMasks make_diag_masks() {
+    DiagMasks t{};
+    for (int d0 = 0; d0 < 2; ++d0)
+        for (int sb = 0; sb < 2; ++sb)
+            for (int r = 0; r < 16; ++r)
+                for (int lane = 0; lane < 64; ++lane) {
+                    const int key = 4 * (lane >> 5) + 32 * sb + 8 * (r >> 2) + (r & 3);
+                    if ((lane & 31) + 32 * d0 >= key) t.m[d0][sb][r] |= uint64_t(1) << lane;
+                }
+    return t;
+}
+constexpr DiagMasks kDiag = make_diag_masks();
+
 struct Params {
     const uint16_t* q;
     const uint16_t* k;
@@ -164,6 +185,19 @@ struct Wave {
     // instruction waits long on the one before it.
     __device__ __forceinline__ bool visible(int j0, int sb, int r) const {
         return j0 + 4 * half + 32 * sb + 8 * (r >> 2) + (r & 3) <= key_lim;
+    }
+
+    // Scores of keys a row does not see on its causal diagonal tile become -inf, in
+    // place (one select per score against a constant lane mask).  The unmasked softmax
+    // then gives them probability exp2(-inf) = 0; c > 0 always (the host passes a tiny
+    // positive c for scale 0), so c * -inf is never NaN.
+    template <int D0>
+    __device__ __forceinline__ void mask_diag(f32x16 (&st)[2]) const {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                st[sb][r] = __builtin_amdgcn_inverse_ballot_w64(kDiag.m[D0 / 32][sb][r]) ? st[sb][r] : kNegInf;
     }
 
     template <bool MASK>
@@ -366,6 +400,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     __syncthreads();  // K buffer 0 may now be refilled
 
     auto is_masked = [&](int j) { return (CAUSAL && j * kBN + kBN - 1 > qw0) || (j * kBN + kBN > N); };
+    // In causal mode the only masked tile of a wavefront is its last, the diagonal tile
+    // j = qw0 / 64, which starts 0 or 32 rows before the wavefront's rows.  Keys at or
+    // past N on it lie above every stored row's diagonal, so the causal mask covers a
+    // ragged end too (rows at or past N compute values that are never stored).
+    auto diag = [&](f32x16(&sc)[2], int j) {
+        if (qw0 == j * kBN) w.template mask_diag<0>(sc);
+        else w.template mask_diag<32>(sc);
+    };
     // GEMM_j (plus, for group 0, the copy of K_{j+2}).  PAR = j % 2 at compile time,
     // so every buffer access names one LDS object.
     // d = 64 halves the matrix work of a tile but not its vector work, so there the
@@ -411,7 +453,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
             if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gwave, k_src);
             if (do_pv) w.pv(vprev);
             if (do_sm) {
-                if (is_masked(j)) {
+                if (CAUSAL && is_masked(j)) {
+                    diag(sc, j);
+                    w.template prep<false>(sc, j0);
+                    w.template exp_half<false, 0>(sc, j0);
+                } else if (is_masked(j)) {
                     w.template prep<true>(sc, j0);
                     w.template exp_half<true, 0>(sc, j0);
                 } else {
@@ -426,11 +472,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     auto softmax = [&](int j, f32x16(&sc)[2]) {
         if (j < 0 || j >= n_w) return;
         if constexpr (SPLIT) {
-            if (is_masked(j)) w.template exp_half<true, 1>(sc, j * kBN);
+            // a causal diagonal tile was masked in place by the matrix half
+            if (!CAUSAL && is_masked(j)) w.template exp_half<true, 1>(sc, j * kBN);
             else w.template exp_half<false, 1>(sc, j * kBN);
             w.finish();
         } else {
-            if (is_masked(j)) {
+            if (CAUSAL && is_masked(j)) {
+                diag(sc, j);
+                w.template prep<false>(sc, j * kBN);
+                w.template expsum<false>(sc, j * kBN);
+            } else if (is_masked(j)) {
                 w.template prep<true>(sc, j * kBN);
                 w.template expsum<true>(sc, j * kBN);
             } else {
@@ -509,7 +560,10 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
     const int64_t blocks = (int64_t)B * H * p.n_qtiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     p.n_blocks = (int)blocks;
-    p.scale_log2 = fabsf(scale) * kLog2e;
+    // c = |scale| log2(e), kept positive: at scale 0 (or below 2^-100) every score times
+    // c rounds away against 1 in exp2, so the weights are still exactly uniform, and a
+    // masked score of -inf still gives probability 0 rather than NaN.
+    p.scale_log2 = fmaxf(fabsf(scale) * kLog2e, 0x1p-100f);
     p.negate_q = scale < 0.0f;  // flipping the sign bit negates exactly in bf16 and in fp16
     if (d == 64) return causal ? launch<64, true, E>(p, st) : launch<64, false, E>(p, st);
     if (d == 128) return causal ? launch<128, true, E>(p, st) : launch<128, false, E>(p, st);
