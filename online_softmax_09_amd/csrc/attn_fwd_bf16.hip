@@ -386,12 +386,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     // and group g runs GEMM_j in half-step 2 j + g and SOFTMAX_j in half-step 2 j + 1 + g.
     // The two wavefronts that share a SIMD are in different groups, so one always has
     // matrix work while the other has vector work.  At half-step 2 j, K_{j+2} (copied
-    // by group 0 during its GEMM) and V_j (copied by group 1 during its SOFTMAX) go
-    // from HBM to the LDS buffers that GEMM_{j-1} finished reading; each has until the
-    // barrier after half-step 2 j + 1 to land.
+    // by group 0 during its GEMM) and V_j (copied by group 1 during its SOFTMAX; V_0
+    // with K_0 and K_1 before the loop) go from HBM to the LDS buffers that GEMM_{j-1}
+    // finished reading; each has until the barrier after half-step 2 j + 1 to land.
     {
         const int ug = __builtin_amdgcn_readfirstlane(group);  // uniform copy of the group
         if (ug == 0 || n_kv > 1) tile_to_lds<D>(ug ? k_lds1 : k_lds0, kh, ug ? kBN : 0, N, gwave, k_src);
+        // V_0 as well, so that its latency overlaps that of Q, K_0 and K_1
+        if (ug == 1) tile_to_lds<D>(v_lds0, vh, 0, N, gwave, v_src);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies have landed
     __syncthreads();
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
         if (group == 0) {
             gemm(par, j, s_cur, s_oth, j + 2 < n_kv);
         } else {
-            if (j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
+            if (j > 0 && j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
             softmax(j - 1, s_oth);
         }
         __syncthreads();
