@@ -10,8 +10,11 @@
 //
 // gfx950 mapping (a design of its own, not the pages' warp/shared-memory scheme):
 //
-//   * Block = 8 wavefronts = 256 query rows; each wavefront owns 32 query rows for
-//     the whole key loop.  Key tiles are 64 keys.  Waves w and w + 4 share a SIMD.
+//   * Each wavefront owns 32 query rows for the whole key loop; key tiles are 64 keys.
+//     Two block forms share the code.  The ping-pong form has 8 wavefronts (256
+//     query rows; waves w and w + 4 share a SIMD) and one block per CU.  The plain
+//     form has 4 wavefronts (128 rows) and two blocks per CU.  The host picks one per
+//     shape (launch_form).
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     A = a 32-key slice of K (from LDS), B = Q^T (held in registers for the whole
 //     loop).  In the 32x32 accumulator, lane l holds one column, i.e. one query row
@@ -32,10 +35,12 @@
 //     XOR-permuted, a permutation chosen so that the 16-byte K reads and the
 //     transposing V reads are free of LDS bank conflicts; a lane fetches the chunk
 //     that belongs at its LDS position.
-//   * Ping-pong between the two wavefronts of each SIMD: the work on a tile is split
-//     into a matrix part (P V of the previous tile, then S of the next) and a vector
-//     part (this tile's softmax), and the two groups of four wavefronts run opposite
-//     parts in each half-step, separated by block barriers.
+//   * The work on a tile is split into a matrix part (P V of the previous tile, then
+//     S of the next) and a vector part (this tile's softmax).  In the ping-pong form
+//     the two groups of four wavefronts run opposite parts in each half-step,
+//     separated by block barriers, so each SIMD has one wavefront on each.  In the
+//     plain form each wavefront runs the two parts in turn, and the two blocks on a CU
+//     share the SIMDs with no common barrier.
 //   * The row's reference maximum m moves lazily: only when a tile's maximum exceeds
 //     it by more than 2^8 (kLazy).  Until then alpha is exactly 1 and the rescale of O
 //     is skipped (decided per wavefront); P stays at most 2^8.  The result O / l and
@@ -55,10 +60,15 @@
 namespace mi355 {
 namespace {
 
-constexpr int kWaves = 8;                  // two groups of four, one of each per SIMD
-constexpr int kThreads = 64 * kWaves;
-constexpr int kGroupThreads = kThreads / 2;
-constexpr int kBM = 32 * kWaves;           // query rows per block
+// Two block forms (PP): 8 wavefronts in two groups of four that ping-pong (one of each
+// group per SIMD, one block per CU), or one group of 4 wavefronts (two blocks per CU).
+template <bool PP>
+constexpr int waves_of() { return PP ? 8 : 4; }
+template <bool PP>
+constexpr int threads_of() { return 64 * waves_of<PP>(); }
+template <bool PP>
+constexpr int rows_of() { return 32 * waves_of<PP>(); }  // query rows per block
+constexpr int kGroupThreads = 256;                       // one group: four wavefronts
 constexpr int kRoundBytes = 16 * kGroupThreads;  // bytes one group-wide 16-byte copy moves
 constexpr int kBN = 64;           // keys per tile
 
@@ -112,6 +122,7 @@ struct Params {
     uint16_t* o;
     float* lse;
     int N;
+    int64_t n_bh;  // B * H
     int n_qtiles;
     int n_blocks;
     float scale_log2;  // |scale| * log2(e)
@@ -296,8 +307,9 @@ struct Wave {
     }
 };
 
-template <int D, bool CAUSAL, typename E>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
+template <int D, bool CAUSAL, typename E, bool PP>
+__global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Params p) {
+    constexpr int kBM = rows_of<PP>();
     using L = Layout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -321,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int group = wave >> 2;  // waves w and w + 4 share a SIMD
+    const int group = PP ? wave >> 2 : 0;  // PP: waves w and w + 4 share a SIMD
     const int gtid = tid & (kGroupThreads - 1);
     // The wavefront's index in its group, read from lane 0 so the compiler knows it is
     // uniform: the LDS copy destinations are then scalar.
@@ -389,11 +401,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     // by group 0 during its GEMM) and V_j (copied by group 1 during its SOFTMAX; V_0
     // with K_0 and K_1 before the loop) go from HBM to the LDS buffers that GEMM_{j-1}
     // finished reading; each has until the barrier after half-step 2 j + 1 to land.
-    {
+    // V_0 goes with K_0 and K_1, so that its latency overlaps theirs and that of Q.
+    if constexpr (PP) {
         const int ug = __builtin_amdgcn_readfirstlane(group);  // uniform copy of the group
         if (ug == 0 || n_kv > 1) tile_to_lds<D>(ug ? k_lds1 : k_lds0, kh, ug ? kBN : 0, N, gwave, k_src);
-        // V_0 as well, so that its latency overlaps that of Q, K_0 and K_1
         if (ug == 1) tile_to_lds<D>(v_lds0, vh, 0, N, gwave, v_src);
+    } else {
+        tile_to_lds<D>(k_lds0, kh, 0, N, gwave, k_src);
+        if (n_kv > 1) tile_to_lds<D>(k_lds1, kh, kBN, N, gwave, k_src);
+        tile_to_lds<D>(v_lds0, vh, 0, N, gwave, v_src);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's copies have landed
     __syncthreads();
@@ -497,19 +513,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     // refills with S_{j+1}.
     auto step = [&](auto par, int j, f32x16(&s_cur)[2], f32x16(&s_oth)[2]) {
         constexpr int PAR = decltype(par)::value;
-        // half-step 2 j
-        if (group == 0) {
+        if constexpr (PP) {
+            // half-step 2 j
+            if (group == 0) {
+                gemm(par, j, s_cur, s_oth, j + 2 < n_kv);
+            } else {
+                if (j > 0 && j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
+                softmax(j - 1, s_oth);
+            }
+            __syncthreads();
+            // half-step 2 j + 1
+            if (group == 0) {
+                softmax(j, s_cur);
+            } else {
+                gemm(par, j, s_cur, s_oth, false);
+            }
+        } else {
+            // one group: GEMM_j (with the copy of K_{j+2}), the copy of V_j, SOFTMAX_j
             gemm(par, j, s_cur, s_oth, j + 2 < n_kv);
-        } else {
             if (j > 0 && j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
-            softmax(j - 1, s_oth);
-        }
-        __syncthreads();
-        // half-step 2 j + 1
-        if (group == 0) {
             softmax(j, s_cur);
-        } else {
-            gemm(par, j, s_cur, s_oth, false);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K_{j+2} and V_j have landed
         __syncthreads();
@@ -542,10 +565,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     }
 }
 
-template <int D, bool CAUSAL, typename E>
-hipError_t launch(const Params& p, hipStream_t st) {
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, E>), dim3((unsigned)p.n_blocks), dim3(kThreads), 0, st, p);
+template <int D, bool CAUSAL, typename E, bool PP>
+hipError_t launch(Params p, hipStream_t st) {
+    p.n_qtiles = (p.N + rows_of<PP>() - 1) / rows_of<PP>();
+    const int64_t blocks = (int64_t)p.n_bh * p.n_qtiles;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    p.n_blocks = (int)blocks;
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, E, PP>), dim3((unsigned)p.n_blocks),
+                       dim3(threads_of<PP>()), 0, st, p);
     return hipGetLastError();
+}
+
+// The block form per shape, from interleaved timings on one MI355X (bitwise identical
+// results either way).  Two 4-wavefront blocks per CU let one block's start, end and
+// causal diagonal run beside the other block's steady state; the ping-pong is faster
+// per key tile once blocks are long.  At d = 128 the two met near causal N = 12288
+// (N / 128 tiles per 256-row block on average) and non-causal N = 3072; at d = 64 the
+// 4-wavefront form was faster at every length timed (2048 to 32768).
+template <int D, bool CAUSAL, typename E>
+hipError_t launch_form(const Params& p, hipStream_t st) {
+    if constexpr (D == 64) {
+        return launch<D, CAUSAL, E, false>(p, st);
+    } else {
+        const bool pp = CAUSAL ? p.N > 10240 : p.N > 3072;
+        return pp ? launch<D, CAUSAL, E, true>(p, st) : launch<D, CAUSAL, E, false>(p, st);
+    }
 }
 
 template <typename E>
@@ -558,17 +602,14 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
     p.o = static_cast<uint16_t*>(o);
     p.lse = lse;
     p.N = N;
-    p.n_qtiles = (N + kBM - 1) / kBM;
-    const int64_t blocks = (int64_t)B * H * p.n_qtiles;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    p.n_blocks = (int)blocks;
+    p.n_bh = (int64_t)B * H;
     // c = |scale| log2(e), kept positive: at scale 0 (or below 2^-100) every score times
     // c rounds away against 1 in exp2, so the weights are still exactly uniform, and a
     // masked score of -inf still gives probability 0 rather than NaN.
     p.scale_log2 = fmaxf(fabsf(scale) * kLog2e, 0x1p-100f);
     p.negate_q = scale < 0.0f;  // flipping the sign bit negates exactly in bf16 and in fp16
-    if (d == 64) return causal ? launch<64, true, E>(p, st) : launch<64, false, E>(p, st);
-    if (d == 128) return causal ? launch<128, true, E>(p, st) : launch<128, false, E>(p, st);
+    if (d == 64) return causal ? launch_form<64, true, E>(p, st) : launch_form<64, false, E>(p, st);
+    if (d == 128) return causal ? launch_form<128, true, E>(p, st) : launch_form<128, false, E>(p, st);
     return hipErrorInvalidValue;
 }
 

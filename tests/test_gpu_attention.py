@@ -292,3 +292,26 @@ def test_score_jumps(d, causal, f, fn, dtype, tol_o, tol_l):
     eo, el = _report(fn, o, lse, o_ref, lse_ref, 1e-3)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     assert eo <= tol_o and el <= tol_l
+
+
+@pytest.mark.parametrize("N,causal", [(3072, False), (3073, False), (10240, True), (10241, True)])
+def test_bf16_both_block_forms(N, causal):
+    """The host runs d = 128 with 4-wavefront blocks (two per CU) up to causal N = 10240
+    and non-causal N = 3072, and with the 8-wavefront ping-pong above; these lengths sit
+    on both sides of each switch.  Sampled rows include both ends and tile edges."""
+    dev = need_gpu()
+    B, H, d = 1, 2, 128
+    q, k, v = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 7400 + N)
+    scale = workloads.default_scale(d)
+    rows = workloads.sampled_query_rows(B, H, N, 96, seed=workloads.SEED_BASE + 7400 + N)
+    edges = np.array([r for r in TILE_EDGES + (N - 2, N - 1) if r < N], dtype=np.int64)
+    rows = np.concatenate([rows, np.broadcast_to(edges, (B, H, len(edges)))], axis=2)
+    say(f"case bf16 block forms N={N} causal={causal}")
+    o, lse = _gpu(osm.fa_fwd, q, k, v, scale, causal, dev)
+    o_ref, lse_ref = oracle_rows_per_head(q, k, v, scale, causal, rows)
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, :, None]
+    eo, el = _report("bf16", o[bi, hi, rows], lse[bi, hi, rows], o_ref, lse_ref, 1e-3)
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    if causal:
+        assert np.array_equal(o[:, :, 0], v[:, :, 0].float().numpy())
