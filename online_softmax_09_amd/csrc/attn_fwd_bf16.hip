@@ -428,12 +428,14 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
     };
     // GEMM_j (plus, for group 0, the copy of K_{j+2}).  PAR = j % 2 at compile time,
     // so every buffer access names one LDS object.
-    // d = 64 halves the matrix work of a tile but not its vector work, so there the
-    // matrix half-step also takes the row maximum of S_j and the exponentials of its
-    // first 32 keys (SPLIT), between its own matrix instructions; the softmax half-step
-    // keeps the other 32 keys.  At d = 128 the two halves are already even and moving
-    // work measured slower.
-    constexpr bool SPLIT = D == 64;
+    // With SPLIT the matrix part also takes the row maximum of S_j and the exponentials
+    // of its first 32 keys, between its own matrix instructions, and the softmax part
+    // keeps the other 32 keys.  In the plain form a wavefront runs both parts itself,
+    // so this overlaps its own vector work with its matrix work.  In the ping-pong form
+    // it evens out the halves at d = 64, where a tile has half the matrix work of
+    // d = 128 but the same vector work; at d = 128 the halves are already even and
+    // moving work there measured slower.
+    constexpr bool SPLIT = D == 64 || !PP;
     auto gemm = [&](auto par, int j, f32x16(&sc)[2], f32x16(&sn)[2], bool copy_k) {
         constexpr int PAR = decltype(par)::value;
         const char* vprev = PAR ? v_lds0 : v_lds1;  // holds V_{j-1}
@@ -579,15 +581,16 @@ hipError_t launch(Params p, hipStream_t st) {
 // The block form per shape, from interleaved timings on one MI355X (bitwise identical
 // results either way).  Two 4-wavefront blocks per CU let one block's start, end and
 // causal diagonal run beside the other block's steady state; the ping-pong is faster
-// per key tile once blocks are long.  At d = 128 the two met near causal N = 12288
-// (N / 128 tiles per 256-row block on average) and non-causal N = 3072; at d = 64 the
-// 4-wavefront form was faster at every length timed (2048 to 32768).
+// per key tile once blocks are long.  At d = 128 the two met near causal N = 16384
+// (N / 128 key tiles per 256-row block on average) and non-causal N = 4096, and the
+// ping-pong led by 1-1.5% at twice those lengths; at d = 64 the 4-wavefront form was
+// faster at every length timed (2048 to 32768).
 template <int D, bool CAUSAL, typename E>
 hipError_t launch_form(const Params& p, hipStream_t st) {
     if constexpr (D == 64) {
         return launch<D, CAUSAL, E, false>(p, st);
     } else {
-        const bool pp = CAUSAL ? p.N > 10240 : p.N > 3072;
+        const bool pp = CAUSAL ? p.N > 16384 : p.N > 4096;
         return pp ? launch<D, CAUSAL, E, true>(p, st) : launch<D, CAUSAL, E, false>(p, st);
     }
 }

@@ -294,10 +294,10 @@ def test_score_jumps(d, causal, f, fn, dtype, tol_o, tol_l):
     assert eo <= tol_o and el <= tol_l
 
 
-@pytest.mark.parametrize("N,causal", [(3072, False), (3073, False), (10240, True), (10241, True)])
+@pytest.mark.parametrize("N,causal", [(4096, False), (4097, False), (16384, True), (16385, True)])
 def test_bf16_both_block_forms(N, causal):
-    """The host runs d = 128 with 4-wavefront blocks (two per CU) up to causal N = 10240
-    and non-causal N = 3072, and with the 8-wavefront ping-pong above; these lengths sit
+    """The host runs d = 128 with 4-wavefront blocks (two per CU) up to causal N = 16384
+    and non-causal N = 4096, and with the 8-wavefront ping-pong above; these lengths sit
     on both sides of each switch.  Sampled rows include both ends and tile edges."""
     dev = need_gpu()
     B, H, d = 1, 2, 128
