@@ -426,8 +426,9 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
         if (qw0 == j * kBN) w.template mask_diag<0>(sc);
         else w.template mask_diag<32>(sc);
     };
-    // GEMM_j (plus, for group 0, the copy of K_{j+2}).  PAR = j % 2 at compile time,
-    // so every buffer access names one LDS object.
+    // GEMM_j (plus the copy of K_{j+2} when copy_k: group 0 in the ping-pong form, the
+    // one group in the plain form).  PAR = j % 2 at compile time, so every buffer access
+    // names one LDS object.
     // With SPLIT the matrix part also takes the row maximum of S_j and the exponentials
     // of its first 32 keys, between its own matrix instructions, and the softmax part
     // keeps the other 32 keys.  In the plain form a wavefront runs both parts itself,
@@ -606,9 +607,10 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
     p.lse = lse;
     p.N = N;
     p.n_bh = (int64_t)B * H;
-    // c = |scale| log2(e), kept positive: at scale 0 (or below 2^-100) every score times
-    // c rounds away against 1 in exp2, so the weights are still exactly uniform, and a
-    // masked score of -inf still gives probability 0 rather than NaN.
+    // c = |scale| log2(e), kept at least 2^-100: at scale 0 every exponent c s - m is then
+    // below 2^-24 in size for any score below 2^76, so exp2 returns exactly 1 and the
+    // weights stay exactly uniform, while a masked score of -inf still gives probability
+    // 0 rather than 0 * -inf = NaN.
     p.scale_log2 = fmaxf(fabsf(scale) * kLog2e, 0x1p-100f);
     p.negate_q = scale < 0.0f;  // flipping the sign bit negates exactly in bf16 and in fp16
     if (d == 64) return causal ? launch_form<64, true, E>(p, st) : launch_form<64, false, E>(p, st);
