@@ -294,24 +294,27 @@ def test_score_jumps(d, causal, f, fn, dtype, tol_o, tol_l):
     assert eo <= tol_o and el <= tol_l
 
 
+@pytest.mark.parametrize("fn,dtype,tol_o,tol_l", [("fa_fwd", "bf16", TOL_BF16_O, TOL_BF16_LSE),
+                                                   ("fa_fwd_f16", "f16", 5e-3, 1e-3)])
 @pytest.mark.parametrize("N,causal", [(4096, False), (4097, False), (16384, True), (16385, True)])
-def test_bf16_both_block_forms(N, causal):
+def test_both_block_forms(N, causal, fn, dtype, tol_o, tol_l):
     """The host runs d = 128 with 4-wavefront blocks (two per CU) up to causal N = 16384
     and non-causal N = 4096, and with the 8-wavefront ping-pong above; these lengths sit
-    on both sides of each switch.  Sampled rows include both ends and tile edges."""
+    on both sides of each switch, in both 16-bit formats.  Sampled rows include both ends
+    and tile edges."""
     dev = need_gpu()
     B, H, d = 1, 2, 128
-    q, k, v = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 7400 + N)
+    q, k, v = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 7400 + N, dtype=dtype)
     scale = workloads.default_scale(d)
     rows = workloads.sampled_query_rows(B, H, N, 96, seed=workloads.SEED_BASE + 7400 + N)
     edges = np.array([r for r in TILE_EDGES + (N - 2, N - 1) if r < N], dtype=np.int64)
     rows = np.concatenate([rows, np.broadcast_to(edges, (B, H, len(edges)))], axis=2)
-    say(f"case bf16 block forms N={N} causal={causal}")
-    o, lse = _gpu(osm.fa_fwd, q, k, v, scale, causal, dev)
+    say(f"case {fn} block forms N={N} causal={causal}")
+    o, lse = _gpu(getattr(osm, fn), q, k, v, scale, causal, dev)
     o_ref, lse_ref = oracle_rows_per_head(q, k, v, scale, causal, rows)
     bi = np.arange(B)[:, None, None]
     hi = np.arange(H)[None, :, None]
-    eo, el = _report("bf16", o[bi, hi, rows], lse[bi, hi, rows], o_ref, lse_ref, 1e-3)
-    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    eo, el = _report(fn, o[bi, hi, rows], lse[bi, hi, rows], o_ref, lse_ref, 1e-3)
+    assert eo <= tol_o and el <= tol_l
     if causal:
         assert np.array_equal(o[:, :, 0], v[:, :, 0].float().numpy())
