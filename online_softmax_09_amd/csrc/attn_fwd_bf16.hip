@@ -498,11 +498,11 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
             else w.template exp_half<false, 1>(sc, j * kBN);
             w.finish();
         } else {
-            if (CAUSAL && is_masked(j)) {
-                diag(sc, j);
-                w.template prep<false>(sc, j * kBN);
-                w.template expsum<false>(sc, j * kBN);
-            } else if (is_masked(j)) {
+            // Only the ping-pong form gets here.  It keeps the per-score mask: sharing the
+            // unmasked code with the lane-mask path split that code into separate
+            // scheduling regions, which cost 1-1.5% on long causal rows, where the
+            // diagonal tile is rare.
+            if (is_masked(j)) {
                 w.template prep<true>(sc, j * kBN);
                 w.template expsum<true>(sc, j * kBN);
             } else {
