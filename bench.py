@@ -365,7 +365,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 disables it)")
     ap.add_argument("--no-next", action="store_true", help="skip the kernels beyond the hot path")
