@@ -600,16 +600,16 @@ hipError_t launch(Params p, hipStream_t st) {
 // The block form per shape, from interleaved timings on one MI355X (bitwise identical
 // results either way).  Two 4-wavefront blocks per CU let one block's start, end and
 // causal diagonal run beside the other block's steady state; the ping-pong is faster
-// per key tile once blocks are long.  At d = 128 the two met between causal N = 12288
-// and 16384 (N / 128 key tiles per 256-row block on average) and near non-causal
-// N = 4096, and the ping-pong led by 1-1.5% at twice those lengths; at d = 64 the
-// 4-wavefront form was faster at every length timed (2048 to 32768).
+// per key tile once blocks are long.  At d = 128 (with the causal head pairs of the
+// kernel's dispatch) the two met near causal N = 10240 (N / 128 key tiles per 256-row
+// block on average) and non-causal N = 4096, and the ping-pong led by 0.5-1.2% above;
+// at d = 64 the 4-wavefront form was faster at every length timed (2048 to 32768).
 template <int D, bool CAUSAL, typename E>
 hipError_t launch_form(const Params& p, hipStream_t st) {
     if constexpr (D == 64) {
         return launch<D, CAUSAL, E, false>(p, st);
     } else {
-        const bool pp = CAUSAL ? p.N > 12288 : p.N > 4096;
+        const bool pp = CAUSAL ? p.N > 10240 : p.N > 4096;
         return pp ? launch<D, CAUSAL, E, true>(p, st) : launch<D, CAUSAL, E, false>(p, st);
     }
 }
