@@ -36,11 +36,11 @@
  *              valid once the caller has synchronised with it.  Nothing here
  *              synchronises.
  *   Errors     Arguments are checked before any HIP call.  A bad argument returns
- *              MI355ATTN_ERR_INVALID_ARG, an unsupported shape or head dimension
- *              returns MI355ATTN_ERR_UNSUPPORTED, and a failed launch returns
- *              MI355ATTN_ERR_HIP (mi355attn_last_hip_error() then gives the
- *              hipError_t of that failure on the calling thread).  On any error no
- *              output has been written.  mi355attn_strerror() names a code.
+ *              FA_ERR_INVALID_ARG, an unsupported shape or head dimension
+ *              returns FA_ERR_UNSUPPORTED, and a failed launch returns FA_ERR_HIP
+ *              (mi355attn_last_hip_error() then gives the hipError_t of that
+ *              failure on the calling thread).  On any error no output has been
+ *              written.  fa_strerror() names a code.
  *   Layout     Dense, row-major, no strides.  Attention tensors are [B, H, N, d]:
  *              element (b, h, n, t) lives at index ((b * H + h) * N + n) * d + t.
  *              LSE is [B, H, N] float32.  Row-softmax tensors are [rows, cols].
@@ -56,11 +56,17 @@
 extern "C" {
 #endif
 
+/* Return codes.  The FA_* names are the boundary's own; the MI355ATTN_* names are the same
+ * values under the library's prefix (kept for callers written against either). */
 enum {
-    MI355ATTN_OK = 0,
-    MI355ATTN_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, bad scale, misaligned or overlapping buffers */
-    MI355ATTN_ERR_UNSUPPORTED = -2, /* head dimension or size the library has no kernel for */
-    MI355ATTN_ERR_HIP = -3          /* the HIP runtime reported an error at launch */
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = -1, /* NULL pointer, bad size, bad scale, misaligned or overlapping buffers */
+    FA_ERR_UNSUPPORTED = -2, /* head dimension or size the library has no kernel for */
+    FA_ERR_HIP = -3,         /* the HIP runtime reported an error at launch */
+    MI355ATTN_OK = FA_OK,
+    MI355ATTN_ERR_INVALID_ARG = FA_ERR_INVALID_ARG,
+    MI355ATTN_ERR_UNSUPPORTED = FA_ERR_UNSUPPORTED,
+    MI355ATTN_ERR_HIP = FA_ERR_HIP
 };
 
 /*
@@ -71,7 +77,7 @@ enum {
  *   lse      [B, H, N] float32, written: ln(sum over visible keys j of exp(scale * q_i . k_j)),
  *            natural log of the scaled scores, = m_i + ln l_i.
  *   B, H, N  >= 1.  N up to 2^31 - 1 (offsets are computed in 64 bits).
- *   d        64 or 128; anything else returns MI355ATTN_ERR_UNSUPPORTED.
+ *   d        64 or 128; anything else returns FA_ERR_UNSUPPORTED.
  *   scale    finite float multiplying every score before the softmax (callers pass 1/sqrt(d)).
  *   causal   0: every query sees all N keys.  1: self-attention, query i sees keys j <= i
  *            (top-left aligned, so no row is empty); tiles wholly above the diagonal are skipped.
@@ -111,8 +117,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  *
  *   x     [rows, cols] float32, read only.
  *   y     [rows, cols] float32, written.  y == x (in place) is allowed; any other overlap is not.
- *   rows  >= 0; rows == 0 does nothing and returns MI355ATTN_OK.
- *   cols  >= 1 and cols <= 1048576 (larger rows return MI355ATTN_ERR_UNSUPPORTED).
+ *   rows  >= 0; rows == 0 does nothing and returns FA_OK.
+ *   cols  >= 1 and cols <= 1048576 (larger rows return FA_ERR_UNSUPPORTED).
  *
  * Each row is read once from device memory when it fits on chip (cols <= 16384) and twice
  * otherwise; it is written once.  Inputs must be finite.
@@ -209,7 +215,7 @@ int attn_merge_states(const float* o_parts, const float* lse_parts, void* o, flo
  *   y             [rows, cols] bf16, written (rounded once, nearest even).
  *   residual_out  [rows, cols] bf16 or NULL: h rounded to bf16 (the updated residual stream).
  *   rows >= 0 (0 does nothing); cols >= 1 and at most 32768 when cols % 8 == 0 and every
- *   pointer is 16-byte aligned, else at most 4096 (longer rows: MI355ATTN_ERR_UNSUPPORTED).
+ *   pointer is 16-byte aligned, else at most 4096 (longer rows: FA_ERR_UNSUPPORTED).
  *   eps finite and >= 0.
  * Pointers need 2-byte alignment.  y and residual_out may each be exactly x or residual (in
  * place); no other overlap is allowed.
@@ -219,10 +225,12 @@ int fused_add_rmsnorm(const void* x, const void* residual, const void* gamma, vo
 int fused_add_layernorm(const void* x, const void* residual, const void* gamma, const void* beta, void* y,
                         void* residual_out, int64_t rows, int64_t cols, float eps, void* stream);
 
-/* Human-readable name of a return code (static string, never NULL). */
+/* Human-readable name of a return code (static string, never NULL).  mi355attn_strerror is
+ * the same function under the library's prefix. */
+const char* fa_strerror(int code);
 const char* mi355attn_strerror(int code);
 
-/* hipError_t of the last MI355ATTN_ERR_HIP returned on the calling thread (0 if none). */
+/* hipError_t of the last FA_ERR_HIP returned on the calling thread (0 if none). */
 int mi355attn_last_hip_error(void);
 
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */

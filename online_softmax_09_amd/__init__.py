@@ -152,11 +152,7 @@ def _check_gpu_tensor(name, t, dtype, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
-def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=1, out=None, lse=None, workspace=None,
-                   stream=None):
-    """bf16 attention of q [B, H, Nq, d] against k, v [B, H, Nk, d] with the keys cut into
-    n_splits parts merged in the log domain; returns (o, lse).  Causal masks are
-    bottom-right aligned (query i sees keys j <= Nk - Nq + i)."""
+def _splitkv_args(q, k, v, scale, out, lse):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_gpu_tensor(name, t, torch.bfloat16, 4)
@@ -174,6 +170,16 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=1, out=None, lse=
     _check_gpu_tensor("lse", lse, torch.float32, 3)
     if out.shape != q.shape or lse.shape != (B, H, Nq):
         raise ValueError("out must be like q and lse [B, H, Nq]")
+    return B, H, Nq, Nk, d, float(scale), out, lse
+
+
+def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=1, out=None, lse=None, workspace=None,
+                   stream=None):
+    """bf16 attention of q [B, H, Nq, d] against k, v [B, H, Nk, d] with the keys cut into
+    n_splits parts merged in the log domain; returns (o, lse).  Causal masks are
+    bottom-right aligned (query i sees keys j <= Nk - Nq + i)."""
+    torch = _torch()
+    B, H, Nq, Nk, d, scale, out, lse = _splitkv_args(q, k, v, scale, out, lse)
     lib = _lib.load()
     need = lib.fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, int(n_splits))
     if need < 0:
@@ -184,7 +190,7 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=1, out=None, lse=
         raise ValueError(f"workspace must be a contiguous float32 tensor of at least {need} bytes")
     with torch.cuda.device(q.device):
         rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                workspace.data_ptr(), B, H, Nq, Nk, d, float(scale), 1 if causal else 0,
+                                workspace.data_ptr(), B, H, Nq, Nk, d, scale, 1 if causal else 0,
                                 int(n_splits), _stream_handle(stream, q.device))
     _lib.check(rc, "fa_fwd_splitkv")
     return out, lse

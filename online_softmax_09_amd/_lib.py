@@ -10,7 +10,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi355attn.so")
 
-# Return codes, as in include/mi355attn.h.
+# Return codes, as in include/mi355attn.h (FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
+# FA_ERR_HIP).
 OK = 0
 ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
@@ -30,6 +31,7 @@ SIGNATURES = {
     "attn_merge_states": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_i64, _c_int, _vp]),
     "fused_add_rmsnorm": (_c_int, [_vp] * 5 + [_c_i64, _c_i64, _c_f, _vp]),
     "fused_add_layernorm": (_c_int, [_vp] * 6 + [_c_i64, _c_i64, _c_f, _vp]),
+    "fa_strerror": (ctypes.c_char_p, [_c_int]),
     "mi355attn_strerror": (ctypes.c_char_p, [_c_int]),
     "mi355attn_last_hip_error": (_c_int, []),
     "mi355attn_version": (_c_int, []),
@@ -55,7 +57,7 @@ def load():
 
 
 def strerror(code):
-    return load().mi355attn_strerror(int(code)).decode()
+    return load().fa_strerror(int(code)).decode()
 
 
 def check(code, what):

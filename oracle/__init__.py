@@ -50,5 +50,5 @@ from .softmax import (  # noqa: F401
 )
 from .attention import attention, attention_rows  # noqa: F401
 from .attention_bwd import attention_backward  # noqa: F401
-from .attention_split import attention_rect, merge_attention_states, split_bounds  # noqa: F401
+from .attention_split import attention_rect, merge_attention_states  # noqa: F401
 from .norms import layer_norm, rms_norm, residual_sum  # noqa: F401

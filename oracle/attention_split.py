@@ -76,10 +76,3 @@ def merge_attention_states(o_parts, lse_parts):
     o = np.sum((w / tot)[..., None] * np.where(np.isfinite(lse_parts)[..., None], o_parts, 0.0), axis=0)
     return o, lse
 
-
-def split_bounds(Nk, n_splits, tile=64):
-    """Key ranges [lo, hi) of the parts a split-KV call uses: chunks of
-    tile * ceil(ceil(Nk / n_splits) / tile) keys; trailing parts may be empty."""
-    per = -(-Nk // n_splits)
-    chunk = tile * (-(-per // tile))
-    return [(min(Nk, s * chunk), min(Nk, (s + 1) * chunk)) for s in range(n_splits)]

@@ -44,6 +44,15 @@ def max_rel(got, ref, floor):
     return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor))) if ref.size else 0.0
 
 
+def split_bounds(Nk, n_splits, tile=64):
+    """Key ranges [lo, hi) of the parts of an fa_fwd_splitkv call, as the C ABI states them:
+    parts of C = tile * ceil(ceil(Nk / n_splits) / tile) keys, trailing parts possibly empty.
+    This is the library's contract, not arithmetic of the method, so it lives with the tests."""
+    per = -(-Nk // n_splits)
+    chunk = tile * (-(-per // tile))
+    return [(min(Nk, s * chunk), min(Nk, (s + 1) * chunk)) for s in range(n_splits)]
+
+
 def oracle_workers():
     try:
         return max(1, min(16, len(os.sched_getaffinity(0))))

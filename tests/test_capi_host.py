@@ -14,6 +14,7 @@ import subprocess
 import pytest
 
 from online_softmax_09_amd import _lib
+from parity import split_bounds
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mi355attn.h")
@@ -46,15 +47,45 @@ def test_every_declared_symbol_is_exported(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in ("fa_fwd", "fa_fwd_f32", "online_softmax_rows", "fa_strerror"):
+        assert name in exported, name
     for name in header_functions():
         assert name in exported, name
         assert hasattr(lib, name)
+    # and no other C symbol leaks out of the library
+    assert {n for n in exported if not n.startswith("_")} == set(header_functions())
+
+
+def header_codes():
+    """Name -> value of every enumerator in the header's return-code enum."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"enum\s*\{(.*?)\}", text, flags=re.S).group(1)
+    codes = {}
+    for item in body.split(","):
+        name, _, value = (t.strip() for t in item.partition("="))
+        codes[name] = codes[value] if value in codes else int(value)
+    return codes
+
+
+def test_return_codes_match_the_boundary():
+    # The boundary's error names and values; the MI355ATTN_* names are aliases.
+    codes = header_codes()
+    assert {k: codes[k] for k in ("FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP")} == {
+        "FA_OK": 0, "FA_ERR_INVALID_ARG": -1, "FA_ERR_UNSUPPORTED": -2, "FA_ERR_HIP": -3}
+    for suffix in ("OK", "ERR_INVALID_ARG", "ERR_UNSUPPORTED", "ERR_HIP"):
+        assert codes["MI355ATTN_" + suffix] == codes["FA_" + suffix]
+    assert (_lib.OK, _lib.ERR_INVALID_ARG, _lib.ERR_UNSUPPORTED, _lib.ERR_HIP) == (0, -1, -2, -3)
 
 
 def test_version_and_strerror(lib):
     assert lib.mi355attn_version() >= 100
     for code in (OK, INVALID, UNSUPPORTED, _lib.ERR_HIP, 12345):
         assert isinstance(_lib.strerror(code), str) and _lib.strerror(code)
+        assert lib.fa_strerror(code) == lib.mi355attn_strerror(code)
+    assert lib.fa_strerror(OK) == b"success"
+    assert b"invalid argument" in lib.fa_strerror(INVALID)
+    assert b"unsupported" in lib.fa_strerror(UNSUPPORTED)
+    assert b"HIP runtime error" in lib.fa_strerror(_lib.ERR_HIP)
     assert lib.mi355attn_last_hip_error() == 0
 
 
@@ -151,6 +182,15 @@ def test_splitkv_argument_checks(lib):
     assert lib.fa_fwd_splitkv_workspace_bytes(1, 2, 3, 128, 0) == -1
 
 
+def test_split_bounds_contract():
+    # The part boundaries the header states for fa_fwd_splitkv (multiples of 64 keys).
+    assert split_bounds(1000, 4) == [(0, 256), (256, 512), (512, 768), (768, 1000)]
+    assert split_bounds(100, 8) == [(0, 64), (64, 100)] + [(100, 100)] * 6
+    assert split_bounds(64, 1) == [(0, 64)]
+    b = split_bounds(131072, 256)
+    assert b[0] == (0, 512) and b[-1] == (130560, 131072)
+
+
 def test_merge_argument_checks(lib):
     f = lib.attn_merge_states
     assert f(A, Bp, C, D, 4, 0, 128, None) == OK          # no rows: nothing to do
@@ -186,3 +226,4 @@ def test_norm_argument_checks(lib):
     assert rms(A, Bp, C, D, E, 4, 32769, 1e-5, None) == UNSUPPORTED
     assert rms(A, Bp, C, D, E, 4, 4097, 1e-5, None) == UNSUPPORTED  # not a multiple of 8
     assert rms(A + 2, Bp, C, D, E, 4, 8192, 1e-5, None) == UNSUPPORTED  # 2-byte units only
+

@@ -15,7 +15,7 @@ import torch
 import online_softmax_09_amd as osm
 import oracle
 import workloads
-from parity import TOL_BF16_LSE, TOL_BF16_O, max_abs, need_gpu, say
+from parity import TOL_BF16_LSE, TOL_BF16_O, max_abs, need_gpu, say, split_bounds
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +100,85 @@ def test_splitkv_deterministic():
     a = _gpu_splitkv(q, k, v, 0.09, True, 17, dev)
     b = _gpu_splitkv(q, k, v, 0.09, True, 17, dev)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,H,Nq,Nk,d,n_splits", [(1, 2, 3, 1000, 128, 4), (1, 1, 5, 300, 64, 16)])
+def test_splitkv_scales(scale, causal, B, H, Nq, Nk, d, n_splits):
+    """The partial kernel's own scale handling (negated Q for a negative scale, c = |scale|
+    log2 e) at scale 0 (uniform weights over the visible keys), a negative scale and a
+    large one.  n_splits = 16 over 300 keys leaves trailing parts empty."""
+    dev = need_gpu()
+    say(f"case splitkv scale={scale} causal={causal} B={B} H={H} Nq={Nq} Nk={Nk} d={d} n_splits={n_splits}")
+    q, k, v = workloads.decode_inputs(B, H, Nq, Nk, d, seed=workloads.SEED_BASE + 8400 + Nk + d)
+    o, lse = _gpu_splitkv(q, k, v, scale, causal, n_splits, dev)
+    o_ref, lse_ref = oracle.attention_rect(q, k, v, scale, causal)
+    eo, el = max_abs(o, o_ref), max_abs(lse, lse_ref)
+    say(f"  O max abs {eo:.3e}  LSE max abs {el:.3e}")
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_merge_states_of_partials_at_scales(scale):
+    """attn_merge_states on partial results the oracle computes over disjoint key ranges
+    (a causal split with empty parts) at the same scales: the merge recovers the oracle's
+    attention over all keys."""
+    dev = need_gpu()
+    say(f"case merge of oracle partials scale={scale}")
+    B, H, Nq, Nk, d, n = 1, 2, 4, 700, 128, 8  # parts of 128 keys: the last two are empty
+    q, k, v = workloads.decode_inputs(B, H, Nq, Nk, d, seed=workloads.SEED_BASE + 8500)
+    qn, kn, vn = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+    rows = B * H * Nq
+    o_parts = np.zeros((n, rows, d))
+    lse_parts = np.full((n, rows), -np.inf)
+    for p, (lo, hi) in enumerate(split_bounds(Nk, n)):
+        for i in range(Nq):
+            e = min(hi, Nk - Nq + i + 1)
+            if e <= lo:
+                continue
+            op, lp = oracle.attention_rect(qn[:, :, i:i + 1], kn[:, :, lo:e], vn[:, :, lo:e], scale, False)
+            o_parts[p, i::Nq] = op.reshape(B * H, d)
+            lse_parts[p, i::Nq] = lp.reshape(B * H)
+    o_ref, lse_ref = oracle.attention_rect(q, k, v, scale, True)
+    o, lse = osm.attn_merge_states(torch.from_numpy(o_parts).float().to(dev),
+                                   torch.from_numpy(lse_parts).float().to(dev))
+    torch.cuda.synchronize()
+    eo = max_abs(o.float().cpu().numpy().reshape(B, H, Nq, d), o_ref)
+    el = max_abs(lse.cpu().numpy().reshape(B, H, Nq), lse_ref)
+    say(f"  O max abs {eo:.3e}  LSE max abs {el:.3e}")
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_splitkv_partials_follow_the_part_contract(causal):
+    """The workspace after a call holds each part's normalised output and LSE over exactly
+    the keys [lo, hi) the header states (64-key multiples), with (0, -inf) for a row that
+    sees no key of its part."""
+    dev = need_gpu()
+    B, H, Nq, Nk, d, n = 1, 2, 5, 1000, 128, 6
+    say(f"case splitkv partials causal={causal} B={B} H={H} Nq={Nq} Nk={Nk} d={d} n_splits={n}")
+    q, k, v = workloads.decode_inputs(B, H, Nq, Nk, d, seed=workloads.SEED_BASE + 8600)
+    scale = workloads.default_scale(d)
+    rows = B * H * Nq
+    ws = torch.empty(osm._lib.load().fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, n) // 4, dtype=torch.float32,
+                     device=dev)
+    osm.fa_fwd_splitkv(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal, n_splits=n, workspace=ws)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy()
+    o_parts = w[:n * rows * d].reshape(n, B, H, Nq, d)
+    lse_parts = w[n * rows * d:n * rows * (d + 1)].reshape(n, B, H, Nq)
+    qn, kn, vn = (t.float().numpy().astype(np.float64) for t in (q, k, v))
+    worst_o = worst_l = 0.0
+    for p, (lo, hi) in enumerate(split_bounds(Nk, n)):
+        for i in range(Nq):
+            e = min(hi, Nk - Nq + i + 1) if causal else hi
+            if e <= lo:
+                assert np.all(lse_parts[p, :, :, i] == -np.inf), (p, i)
+                assert np.all(o_parts[p, :, :, i] == 0.0), (p, i)
+                continue
+            op, lp = oracle.attention_rect(qn[:, :, i:i + 1], kn[:, :, lo:e], vn[:, :, lo:e], scale, False)
+            worst_o = max(worst_o, max_abs(o_parts[p, :, :, i], op[:, :, 0]))
+            worst_l = max(worst_l, max_abs(lse_parts[p, :, :, i], lp[:, :, 0]))
+    say(f"  partial O max abs {worst_o:.3e}  partial LSE max abs {worst_l:.3e}")
+    assert worst_o <= TOL_BF16_O and worst_l <= TOL_BF16_LSE

@@ -132,14 +132,6 @@ def test_merge_closed_forms():
     assert check_merge_closed_forms(oracle.merge_attention_states)
 
 
-def test_split_bounds():
-    assert oracle.split_bounds(1000, 4) == [(0, 256), (256, 512), (512, 768), (768, 1000)]
-    assert oracle.split_bounds(100, 8) == [(0, 64), (64, 100)] + [(100, 100)] * 6
-    assert oracle.split_bounds(64, 1) == [(0, 64)]
-    b = oracle.split_bounds(131072, 256)
-    assert b[0] == (0, 512) and b[-1] == (130560, 131072)
-
-
 def test_rejects_bad_input():
     with pytest.raises(ValueError):
         oracle.attention_rect(np.zeros((1, 1, 5, 4)), np.zeros((1, 1, 3, 4)), np.zeros((1, 1, 3, 4)), 1.0, True)
