@@ -30,7 +30,9 @@
  *
  *   Memory     All pointers are device pointers to memory owned by the caller.  The
  *              library allocates, frees and copies nothing, keeps no global mutable
- *              state, and may be called from several host threads at once.
+ *              state, and may be called from several host threads at once.  The one
+ *              exception is fa_fwd_splitkv_noalloc, whose device-resident scratch is
+ *              shared by its calls on a device (see there).
  *   Streams    `stream` is a hipStream_t passed as void*; NULL means the default
  *              stream.  Work is enqueued asynchronously on that stream; outputs are
  *              valid once the caller has synchronised with it.  Nothing here
@@ -183,6 +185,28 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 
 /* Bytes of workspace fa_fwd_splitkv needs: n_splits * B*H*Nq * (d + 1) * 4; -1 on bad sizes. */
 int64_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int d, int n_splits);
+
+/*
+ * fa_fwd_splitkv_noalloc — fa_fwd_splitkv for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * It takes no workspace.  The partial results go to a scratch array that the library keeps
+ * in device memory, 32 MiB (33554432 bytes) per device, held from the first call on that
+ * device until the process ends.  Nothing in this call allocates or frees memory.
+ *
+ *   Arguments, layout, results and errors as for fa_fwd_splitkv, without workspace.
+ *   A call whose partials would need more than the scratch holds,
+ *   fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits) > 33554432, returns
+ *   FA_ERR_UNSUPPORTED before any HIP call (fewer splits or fewer queries per call fit).
+ *
+ * Every call on one device shares that device's scratch, and each call fully rewrites the
+ * part it reads, so nothing carries over from an earlier call.  Calls that may run at the
+ * same time on one device (on different streams, or from several host threads without
+ * ordering) race on the scratch and are not allowed; calls on one stream are ordered.
+ * The first call on a device looks up the scratch address with that device current.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Nq, int Nk, int d, float scale, int causal, int n_splits,
+                           void* stream);
 
 /*
  * attn_merge_states — merges partial attention results computed over disjoint key sets

@@ -16,6 +16,8 @@ Functions carry the names of the C entry points:
   of ``fa_fwd`` for the upstream gradient ``dout``
 * ``fa_fwd_splitkv(q, k, v, scale, causal, n_splits)``  bf16 q [B, H, Nq, d] against
   k, v [B, H, Nk, d] -> (o, lse), keys cut into parts merged in the log domain
+* ``fa_fwd_splitkv_noalloc(q, k, v, scale, causal, n_splits)``  the same with the partial
+  results in the library's own per-device scratch (no workspace, nothing allocated)
 * ``attn_merge_states(o_parts, lse_parts)``  float32 partial results -> (o bf16, lse)
 * ``fused_add_rmsnorm(x, residual, gamma, eps)`` / ``fused_add_layernorm(x, residual, gamma,
   beta, eps)``  bf16 [rows, cols] -> (y, h = x + residual)
@@ -25,7 +27,8 @@ import math
 
 from . import _lib
 
-__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_fwd_splitkv", "attn_merge_states", "online_softmax_rows",
+__all__ = ["fa_fwd", "fa_fwd_f16", "fa_fwd_f32", "fa_bwd", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc",
+           "attn_merge_states", "online_softmax_rows",
            "fused_add_rmsnorm", "fused_add_layernorm", "library_path", "version"]
 
 
@@ -193,6 +196,20 @@ def fa_fwd_splitkv(q, k, v, scale=None, causal=False, n_splits=1, out=None, lse=
                                 workspace.data_ptr(), B, H, Nq, Nk, d, scale, 1 if causal else 0,
                                 int(n_splits), _stream_handle(stream, q.device))
     _lib.check(rc, "fa_fwd_splitkv")
+    return out, lse
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, scale=None, causal=False, n_splits=1, out=None, lse=None, stream=None):
+    """fa_fwd_splitkv with the partial results in the library's per-device scratch instead
+    of a workspace (the C entry point allocates nothing; pass out and lse to keep this
+    wrapper from allocating them).  Calls that overlap on one device race."""
+    torch = _torch()
+    B, H, Nq, Nk, d, scale, out, lse = _splitkv_args(q, k, v, scale, out, lse)
+    with torch.cuda.device(q.device):
+        rc = _lib.load().fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                lse.data_ptr(), B, H, Nq, Nk, d, scale, 1 if causal else 0,
+                                                int(n_splits), _stream_handle(stream, q.device))
+    _lib.check(rc, "fa_fwd_splitkv_noalloc")
     return out, lse
 
 

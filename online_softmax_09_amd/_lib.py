@@ -17,6 +17,9 @@ ERR_INVALID_ARG = -1
 ERR_UNSUPPORTED = -2
 ERR_HIP = -3
 
+# Bytes of device scratch fa_fwd_splitkv_noalloc holds per device.
+SPLITKV_SCRATCH_BYTES = 32 << 20
+
 # Every symbol the header declares, with (restype, argtypes).
 _c_int, _c_i64, _c_f, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 SIGNATURES = {
@@ -28,6 +31,7 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_c_i64, [_c_int, _c_int, _c_int]),
     "fa_fwd_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 5 + [_c_f, _c_int, _c_int, _vp]),
     "fa_fwd_splitkv_workspace_bytes": (_c_i64, [_c_int] * 5),
+    "fa_fwd_splitkv_noalloc": (_c_int, [_vp] * 5 + [_c_int] * 5 + [_c_f, _c_int, _c_int, _vp]),
     "attn_merge_states": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_i64, _c_int, _vp]),
     "fused_add_rmsnorm": (_c_int, [_vp] * 5 + [_c_i64, _c_i64, _c_f, _vp]),
     "fused_add_layernorm": (_c_int, [_vp] * 6 + [_c_i64, _c_i64, _c_f, _vp]),

@@ -171,6 +171,16 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                                                   scale, causal != 0, n_splits, static_cast<hipStream_t>(stream)));
 }
 
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                           int Nk, int d, float scale, int causal, int n_splits, void* stream) {
+    const int rc = check_splitkv(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, n_splits);
+    if (rc != FA_OK) return rc;
+    if (fa_fwd_splitkv_workspace_bytes(B, H, Nq, d, n_splits) > mi355::kSplitkvScratchBytes)
+        return FA_ERR_UNSUPPORTED;
+    return finish(mi355::launch_attn_splitkv_bf16_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal != 0,
+                                                          n_splits, static_cast<hipStream_t>(stream)));
+}
+
 int attn_merge_states(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts, int64_t rows,
                       int d, void* stream) {
     if (rows < 0 || n_parts < 1 || n_parts > 65536 || d < 1) return FA_ERR_INVALID_ARG;

@@ -26,9 +26,17 @@
 // parts.  Each thread takes the maximum LSE of its share, then sums e^{LSE_p - max} O_p
 // and e^{LSE_p - max} over it (independent loads, unrolled), and the shares are merged
 // through LDS with the two-state rule.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launchers.hpp"
 #include "mfma_bf16.hpp"
+
+// Device-resident scratch of the allocation-free split-KV entry point: the partial
+// results that fa_fwd_splitkv otherwise keeps in the caller's workspace.  Each device
+// the library runs on holds its own copy for the life of the process.  In host code the
+// name is only a stand-in; kernels receive the address hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[mi355::kSplitkvScratchBytes / sizeof(float)];
 
 namespace mi355 {
 namespace {
@@ -354,6 +362,46 @@ hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v,
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_attn_merge(p.o_part, p.lse_part, o, lse, n_parts, p.rows, d, st);
+}
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept.
+constexpr int kMaxDevices = 64;
+
+hipError_t scratch_address(float** out) {
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float*>(ptr);
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_attn_splitkv_bf16_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                            int B, int H, int Nq, int Nk, int d, float scale, bool causal,
+                                            int n_parts, hipStream_t st) {
+    const int64_t need = (int64_t)n_parts * B * H * Nq * (int64_t)(d + 1) * (int64_t)sizeof(float);
+    if (need > kSplitkvScratchBytes) return hipErrorInvalidValue;  // the C ABI rejects this first
+    float* ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    // Every partial row of every part is written by the partial kernel before the merge
+    // reads it (an empty part writes O = 0 and LSE = -inf), so nothing is cleared.
+    return launch_attn_splitkv_bf16(q, k, v, o, lse, ws, B, H, Nq, Nk, d, scale, causal, n_parts, st);
 }
 
 }  // namespace mi355

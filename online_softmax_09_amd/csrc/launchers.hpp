@@ -39,6 +39,13 @@ hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v,
                                     float* workspace, int B, int H, int Nq, int Nk, int d, float scale, bool causal,
                                     int n_parts, hipStream_t st);
 
+// The same with the partials in the library's own device-resident scratch of
+// kSplitkvScratchBytes per device (no allocation; calls that overlap on one device race).
+constexpr int64_t kSplitkvScratchBytes = int64_t(32) << 20;
+hipError_t launch_attn_splitkv_bf16_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                            int B, int H, int Nq, int Nk, int d, float scale, bool causal,
+                                            int n_parts, hipStream_t st);
+
 hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts,
                              int64_t rows, int d, hipStream_t st);
 

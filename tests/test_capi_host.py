@@ -227,3 +227,27 @@ def test_norm_argument_checks(lib):
     assert rms(A, Bp, C, D, E, 4, 4097, 1e-5, None) == UNSUPPORTED  # not a multiple of 8
     assert rms(A + 2, Bp, C, D, E, 4, 8192, 1e-5, None) == UNSUPPORTED  # 2-byte units only
 
+
+def _skv_na(lib, q=A, k=Bp, v=C, o=D, lse=E, B=1, H=2, Nq=3, Nk=100, d=128, scale=0.1, causal=1, n=4):
+    return lib.fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, n, None)
+
+
+def test_splitkv_noalloc_argument_checks(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert _skv_na(lib, **{name: None}) == INVALID, name
+    for bad in (dict(B=0), dict(H=0), dict(Nq=0), dict(Nk=0), dict(d=0), dict(n=0), dict(n=4097),
+                dict(causal=2), dict(Nq=101, Nk=100)):
+        assert _skv_na(lib, **bad) == INVALID, bad
+    assert _skv_na(lib, scale=math.inf) == INVALID
+    assert _skv_na(lib, o=A + 16) == INVALID            # o overlaps q
+    assert _skv_na(lib, lse=D + 32) == INVALID          # lse overlaps o
+    assert _skv_na(lib, d=96) == UNSUPPORTED
+    # partials beyond the 32 MiB scratch are refused before any HIP call
+    limit = _lib.SPLITKV_SCRATCH_BYTES
+    assert limit == 32 << 20
+    H, Nq, d = 32, 16, 128
+    fits = limit // (H * Nq * (d + 1) * 4)                      # 127 parts fit, 128 do not
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, H, Nq, d, fits) <= limit
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, H, Nq, d, fits + 1) > limit
+    assert _skv_na(lib, H=H, Nq=Nq, Nk=32768, n=fits + 1) == UNSUPPORTED
+    assert _skv_na(lib, B=4, H=H, Nq=Nq, Nk=32768, n=fits) == UNSUPPORTED
