@@ -19,8 +19,11 @@
 //     A = a 32-key slice of K (from LDS), B = Q^T (held in registers for the whole
 //     loop).  In the 32x32 accumulator, lane l holds one column, i.e. one query row
 //     (l mod 32), and 16 of its keys; the other 16 keys of that row sit in lane l^32.
-//     So the row max is in-lane maxima plus one exchange, and the row sum needs no
-//     exchange at all until the end (each half keeps a partial l under the same m).
+//     So the row max is in-lane maxima plus one exchange.
+//   * The row sum l is formed on the matrix cores as well: a 16x16x32 product of a 0/1
+//     selection matrix with the packed P^T fragments adds each query's probabilities
+//     (the same bf16 values that P V uses) into an accumulator that holds l for the
+//     lane's own query row, so l costs no vector instruction per score.
 //   * The output is accumulated transposed too, O^T += V^T P^T: the B operand
 //     (P^T, 8 keys x 1 query per lane) is exactly what the lane already holds after
 //     the exponentials, converted to bf16 with no data movement.  V is kept in LDS
@@ -165,14 +168,14 @@ struct Wave {
     v8 qf[KS];       // Q^T fragments (B operand of S^T = K Q^T)
     f32x16 acc[DB];  // O^T accumulator: this lane's query row, 16 of each 32 outputs
     v8 pf[4];        // P^T fragments of the last finished tile (B operand of O^T += V^T P^T)
+    v8 sel;          // A operand of the row sums (0/1 selection, see rowsum)
+    f32x4 lacc;      // row-sum accumulator: element 0 = l of this lane's query row
     int k_off[KS];   // byte offset of this lane's K fragment for k-step ks (row l32)
     int v_off[DB];   // byte offset of this lane's transposing V block for output block b
     float m;         // reference max of |scale| log2(e) score, this lane's row (see kLazy)
-    float l;         // running partial sum over this lane's half of every tile
     float c;         // |scale| log2(e)
     float base;      // finite stand-in for m while a tile is exponentiated
     float alpha;     // exp2(m_old - m_new) of the tile in flight
-    float psum[4];   // partial row sums of the tile in flight (split softmax, d = 64)
     int half, key_lim;
 
     // S^T = K Q^T for the two 32-key halves of a tile (A = K rows from LDS).
@@ -192,9 +195,10 @@ struct Wave {
     // Online-softmax update of one tile, in two parts.  prep (reads S only): the row
     // maximum over the visible keys is taken and moves the reference m if it exceeds it
     // by more than kLazy.  expsum: the 32 keys are exponentiated (hidden keys, on
-    // diagonal or ragged tiles only, get exactly 0), summed into l and packed to bf16
-    // P^T fragments.  Reductions run as four independent partial chains so that no
-    // instruction waits long on the one before it.
+    // diagonal or ragged tiles only, get exactly 0) and packed to bf16 P^T fragments,
+    // which the matrix part then multiplies into O and sums into l.  The maximum runs
+    // as four independent partial chains so that no instruction waits long on the one
+    // before it.
     __device__ __forceinline__ bool visible(int j0, int sb, int r) const {
         return j0 + 4 * half + 32 * sb + 8 * (r >> 2) + (r & 3) <= key_lim;
     }
@@ -227,13 +231,10 @@ struct Wave {
         base = safe_base(m_new);
         alpha = fast_exp2(m - base);  // 1 when m stays; 0 when m = -inf
         m = m_new;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) psum[i] = 0.0f;
     }
 
     template <bool MASK>
     __device__ __forceinline__ void expsum(f32x16 (&st)[2], int j0) {
-        float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -241,9 +242,7 @@ struct Wave {
                 float e = fast_exp2(fmaf(st[sb][r], c, -base));
                 if (MASK) e = visible(j0, sb, r) ? e : 0.0f;
                 st[sb][r] = e;
-                sum[r & 3] += e;
             }
-        l = alpha * l + ((sum[0] + sum[1]) + (sum[2] + sum[3]));
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -256,10 +255,9 @@ struct Wave {
             }
     }
 
-    // The same work split in two for d = 64 (see the kernel): the exponentials of one
-    // 32-key half, summed into psum and packed straight into the P^T fragments (the
-    // previous tile's fragments must have been consumed), then the update of l.  The
-    // arithmetic and its order are those of expsum.
+    // The same work split in two (see the kernel): the exponentials of one 32-key half,
+    // packed straight into the P^T fragments (the previous tile's fragments must have
+    // been consumed).  The arithmetic and its order are those of expsum.
     template <bool MASK, int SB>
     __device__ __forceinline__ void exp_half(f32x16 (&st)[2], int j0) {
 #pragma unroll
@@ -267,7 +265,6 @@ struct Wave {
             float e = fast_exp2(fmaf(st[SB][r], c, -base));
             if (MASK) e = visible(j0, SB, r) ? e : 0.0f;
             st[SB][r] = e;
-            psum[r & 3] += e;
         }
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -277,16 +274,28 @@ struct Wave {
             pf[2 * SB + hb] = __builtin_bit_cast(v8, w);
         }
     }
-    __device__ __forceinline__ void finish() { l = alpha * l + ((psum[0] + psum[1]) + (psum[2] + psum[3])); }
-
-    // O^T *= alpha, skipped (per wavefront) when no row moved its reference maximum.
+    // O^T *= alpha and l *= alpha, skipped (per wavefront) when no row moved its
+    // reference maximum.
     __device__ __forceinline__ void rescale() {
         if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
             for (int b = 0; b < DB; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lacc[i] *= alpha;
         }
+    }
+
+    // l += the row sums of the packed P^T fragments, on the matrix cores: in the
+    // 16x16x32 product lane l supplies B[8 (l / 16) + i][l % 16], i.e. query l % 32 in
+    // the lanes whose l / 16 is even for n = l % 16 and odd for n = l % 16 + 16.  The
+    // selection rows 0 and 8 add the even groups, rows 4 and 12 the odd ones, so element
+    // 0 of the output (row 4 (l / 16), column l % 16) is the sum for query l % 32 in
+    // every lane.  l is then the sum of the same bf16 P that P V uses.
+    __device__ __forceinline__ void rowsum() {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) lacc = E::mfma16(sel, pf[g], lacc);
     }
 
     // O^T += V^T P^T with the packed P of the last finished tile.  A operand for
@@ -376,7 +385,13 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
     w.key_lim = CAUSAL ? min(N - 1, my_q) : N - 1;  // last visible key of the row
     w.c = p.scale_log2;
     w.m = kNegInf;
-    w.l = 0.0f;
+    w.lacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    {
+        const int m16 = lane & 15, kb = lane >> 4;
+        const bool one = ((m16 == 0 || m16 == 8) && (kb & 1) == 0) || ((m16 == 4 || m16 == 12) && (kb & 1) == 1);
+        const uint32_t wv = one ? E::kOnes2 : 0u;
+        w.sel = __builtin_bit_cast(typename E::v8, u32x4{wv, wv, wv, wv});
+    }
     // K fragment of lane l: row l32 (+32 sb) of the tile, logical chunk 2 ks + half.
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) w.k_off[ks] = l32 * L::RB + 16 * ((2 * ks + w.half) ^ L::k_swz(l32));
@@ -445,8 +460,9 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
         else w.template mask_diag<32>(sc);
     };
     // GEMM_j (plus the copy of K_{j+2} when copy_k: group 0 in the ping-pong form, the
-    // one group in the plain form).  PAR = j % 2 at compile time, so every buffer access
-    // names one LDS object.
+    // one group in the plain form; and the copy of V_j when copy_v: the plain form, where
+    // issuing it here rather than after the matrix part gives it a whole tile to land).
+    // PAR = j % 2 at compile time, so every buffer access names one LDS object.
     // With SPLIT the matrix part also takes the row maximum of S_j and the exponentials
     // of its first 32 keys, between its own matrix instructions, and the softmax part
     // keeps the other 32 keys.  In the plain form a wavefront runs both parts itself,
@@ -455,7 +471,7 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
     // d = 128 but the same vector work; at d = 128 the halves are already even and
     // moving work there measured slower.
     constexpr bool SPLIT = D == 64 || !PP;
-    auto gemm = [&](auto par, int j, f32x16(&sc)[2], f32x16(&sn)[2], bool copy_k) {
+    auto gemm = [&](auto par, int j, f32x16(&sc)[2], f32x16(&sn)[2], bool copy_k, bool copy_v) {
         constexpr int PAR = decltype(par)::value;
         const char* vprev = PAR ? v_lds0 : v_lds1;  // holds V_{j-1}
         const char* knext = PAR ? k_lds0 : k_lds1;  // holds K_{j+1}
@@ -466,7 +482,9 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
         __builtin_amdgcn_s_setprio(1);
         if (do_pv && do_qk && !(SPLIT && is_masked(j))) {
             if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gwave, k_src);
+            if (copy_v) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
             w.pv(vprev);
+            w.rowsum();
             if constexpr (SPLIT) w.template prep<false>(sc, j0);
             w.qk(sn, knext);
             if constexpr (SPLIT) w.template exp_half<false, 0>(sc, j0);
@@ -475,11 +493,11 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
             // instructions.
             __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 20; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (i < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 if (SPLIT) __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-                if (i % 4 == 3) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                if (i % 4 == 3 && i < 16) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -490,7 +508,11 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
             }
         } else {
             if (copy_k) tile_to_lds<D>(PAR ? k_lds1 : k_lds0, kh, (j + 2) * kBN, N, gwave, k_src);
-            if (do_pv) w.pv(vprev);
+            if (copy_v) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
+            if (do_pv) {
+                w.pv(vprev);
+                w.rowsum();
+            }
             if (do_sm) {
                 if (CAUSAL && is_masked(j)) {
                     diag(sc, j);
@@ -514,7 +536,6 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
             // a causal diagonal tile was masked in place by the matrix half
             if (!CAUSAL && is_masked(j)) w.template exp_half<true, 1>(sc, j * kBN);
             else w.template exp_half<false, 1>(sc, j * kBN);
-            w.finish();
         } else {
             // Only the ping-pong form gets here.  It keeps the per-score mask: sharing the
             // unmasked code with the lane-mask path split that code into separate
@@ -537,7 +558,7 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
         if constexpr (PP) {
             // half-step 2 j
             if (group == 0) {
-                gemm(par, j, s_cur, s_oth, j + 2 < n_kv);
+                gemm(par, j, s_cur, s_oth, j + 2 < n_kv, false);
             } else {
                 if (j > 0 && j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
                 softmax(j - 1, s_oth);
@@ -547,12 +568,11 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
             if (group == 0) {
                 softmax(j, s_cur);
             } else {
-                gemm(par, j, s_cur, s_oth, false);
+                gemm(par, j, s_cur, s_oth, false, false);
             }
         } else {
-            // one group: GEMM_j (with the copy of K_{j+2}), the copy of V_j, SOFTMAX_j
-            gemm(par, j, s_cur, s_oth, j + 2 < n_kv);
-            if (j > 0 && j < n_kv) tile_to_lds<D>(PAR ? v_lds1 : v_lds0, vh, j * kBN, N, gwave, v_src);
+            // one group: GEMM_j (with the copies of K_{j+2} and V_j), SOFTMAX_j
+            gemm(par, j, s_cur, s_oth, j + 2 < n_kv, j > 0 && j < n_kv);
             softmax(j, s_cur);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K_{j+2} and V_j have landed
@@ -567,8 +587,7 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
     if (j <= n_kv) step(std::integral_constant<int, 0>{}, j, sa, sb);
 
     if (!wave_live) return;
-    const HalfPair pl = half_pair(w.l);
-    const float l_row = pl.lo + pl.hi;
+    const float l_row = w.lacc[0];
     if (my_q < N) {
         const float inv = 1.0f / l_row;
         uint16_t* orow = p.o + head + (int64_t)my_q * D;

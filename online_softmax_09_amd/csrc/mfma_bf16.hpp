@@ -43,23 +43,32 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const char* p_lo, const char*
 }
 
 // The two 16-bit input formats of the attention kernels: the 8-element operand vector of
-// v_mfma_f32_32x32x16_{bf16,f16}, the product itself, and float -> 16-bit packing
-// (round to nearest even).
+// v_mfma_f32_32x32x16_{bf16,f16}, the product itself, the 16x16x32 product with the same
+// operand vectors, two 16-bit ones packed in a word, and float -> 16-bit packing (round
+// to nearest even).
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct ElemBF16 {
     using v8 = bf16x8;
+    static constexpr uint32_t kOnes2 = 0x3F803F80u;
     __device__ static __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
     __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
 };
 
 struct ElemF16 {
     using v8 = f16x8;
+    static constexpr uint32_t kOnes2 = 0x3C003C00u;
     __device__ static __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
     __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
