@@ -8,7 +8,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmi355attn.so")
+# The in-tree library.  MI355ATTN_LIB_PATH names another build of the same C ABI (the
+# tests use it for a host-only AddressSanitizer build of the argument checks).
+LIB_PATH = os.environ.get("MI355ATTN_LIB_PATH") or os.path.join(_HERE, "libmi355attn.so")
 
 # Return codes, as in include/mi355attn.h (FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
 # FA_ERR_HIP).

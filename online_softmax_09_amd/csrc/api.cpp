@@ -3,7 +3,7 @@
 // Every argument is validated here, before any HIP call, so bad input comes back as a
 // return code without touching the device.  The launchers enqueue on the caller's
 // stream and never synchronise.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <climits>
 #include <cmath>

@@ -3,7 +3,7 @@
 // its launch.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace mi355 {
@@ -52,6 +52,11 @@ hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, void*
 // Residual add + LayerNorm (layer) or RMSNorm of bf16 rows.  res, beta (RMSNorm) and
 // res_out may be null.  norm_rows_max_cols gives the longest row the launch accepts for
 // these pointers (rows of a multiple of 8 with 16-byte aligned pointers use 16-byte units).
+// Threads per row block of the norm kernel.  norm_vec_path: whether a call takes the
+// 16-byte path (host logic in host_plan.cpp, shared by the argument checks and the launch).
+constexpr int kNormRowThreads = 256;
+bool norm_vec_path(bool layer, const void* x, const void* res, const void* gamma, const void* beta, const void* y,
+                   const void* res_out, int64_t cols);
 int64_t norm_rows_max_cols(bool layer, const void* x, const void* res, const void* gamma, const void* beta,
                            const void* y, const void* res_out, int64_t cols);
 hipError_t launch_norm_rows(bool layer, const void* x, const void* res, const void* gamma, const void* beta, void* y,

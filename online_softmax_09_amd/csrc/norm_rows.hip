@@ -29,7 +29,7 @@
 namespace mi355 {
 namespace {
 
-constexpr int kNormThreads = 256;
+constexpr int kNormThreads = kNormRowThreads;
 
 struct NormParams {
     const uint16_t* x;
@@ -192,20 +192,7 @@ hipError_t launch_u(const NormParams& p, int64_t rows, int nv, hipStream_t st) {
     return hipGetLastError();
 }
 
-bool aligned16(const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) == 0; }
-
-bool norm_vec_path(bool layer, const void* x, const void* res, const void* gamma, const void* beta, const void* y,
-                   const void* res_out, int64_t cols) {
-    return cols % 8 == 0 && aligned16(x) && aligned16(y) && aligned16(gamma) && (!res || aligned16(res)) &&
-           (!res_out || aligned16(res_out)) && (!layer || aligned16(beta));
-}
-
 }  // namespace
-
-int64_t norm_rows_max_cols(bool layer, const void* x, const void* res, const void* gamma, const void* beta,
-                           const void* y, const void* res_out, int64_t cols) {
-    return norm_vec_path(layer, x, res, gamma, beta, y, res_out, cols) ? 16 * kNormThreads * 8 : 16 * kNormThreads;
-}
 
 hipError_t launch_norm_rows(bool layer, const void* x, const void* res, const void* gamma, const void* beta, void* y,
                             void* res_out, int64_t rows, int64_t cols, float eps, hipStream_t st) {
