@@ -21,11 +21,10 @@
 // by the transposing LDS load.  The running maximum follows the pages' rule exactly
 // (moved at every sub-tile); O is rescaled only when some row's maximum moved.
 //
-// Merge kernel: one block per query row (1024 threads when there are few rows, else
-// 256); threads own output columns and a share of the
-// parts.  Each thread takes the maximum LSE of its share, then sums e^{LSE_p - max} O_p
-// and e^{LSE_p - max} over it (independent loads, unrolled), and the shares are merged
-// through LDS with the two-state rule.
+// Merge kernel: one block of 256 threads per query row; threads own a 16-byte chunk of
+// the output columns and a lane of the parts.  The row's LSEs are read once (and staged
+// in LDS) for the maximum, then every part's output chunk is summed with the weight
+// e^{LSE_p - max} (independent loads, unrolled), and the lanes' sums add up through LDS.
 #include <mutex>
 
 #include "device_common.hpp"
@@ -260,55 +259,77 @@ __global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams
 }
 
 // ---------------------------------------------------------------------------------
-// Merge: one block of G * D threads per row; thread t owns column t % D of part share
-// t / D (parts share, share + G, ...).
+// Merge: one block of 256 threads per row.  Thread t owns the 16-byte column chunk
+// c = t % (D / 4) of part lane t / (D / 4) (parts lane, lane + lanes, ...).  Two rounds of
+// independent loads: every part's LSE (staged in LDS as LSE log2 e), the block maximum,
+// then every part's output chunk weighted by e^{LSE_p - max}; the lanes' sums then add
+// up through LDS.  All weights share the block maximum, so no lane rescales another.
 // ---------------------------------------------------------------------------------
-template <int D, int G>
-__global__ __launch_bounds__(G * D) void attn_merge_kernel(const float* o_parts, const float* lse_parts, uint16_t* o,
-                                                           float* lse, int n_parts, int64_t rows) {
-    __shared__ float sm_m[G][D], sm_l[G][D], sm_a[G][D];
+constexpr int kMergeThreads = 256;
+constexpr int kMergeStaged = 2048;  // parts whose LSE stays in LDS between the passes
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* o_parts, const float* lse_parts,
+                                                                   uint16_t* o, float* lse, int n_parts,
+                                                                   int64_t rows) {
+    constexpr int C = D / 4;                  // 16-byte chunks per row
+    constexpr int LANES = kMergeThreads / C;  // part lanes
+    __shared__ float sm_lse[kMergeStaged];
+    __shared__ float sm_max[kMergeThreads / 64];
+    __shared__ f32x4 sm_acc[LANES][C];
+    __shared__ float sm_w[LANES];
     const int64_t row = blockIdx.x;
-    const int col = threadIdx.x % D, share = threadIdx.x / D;
-    float m = kNegInf, l = 0.0f, a = 0.0f;
-    for (int pidx = share; pidx < n_parts; pidx += G) m = fmaxf(m, lse_parts[(int64_t)pidx * rows + row] * kLog2e);
-    const float base = safe_base(m);
-#pragma unroll 8
-    for (int pidx = share; pidx < n_parts; pidx += G) {
-        const float w = fast_exp2(lse_parts[(int64_t)pidx * rows + row] * kLog2e - base);  // 0 for empty parts
-        const float x = o_parts[((int64_t)pidx * rows + row) * D + col];
-        a = fmaf(w, w > 0.0f ? x : 0.0f, a);
-        l += w;
+    const int t = threadIdx.x, c = t % C, lane = t / C;
+
+    float m = kNegInf;
+    for (int pidx = t; pidx < n_parts; pidx += kMergeThreads) {
+        const float x = lse_parts[(int64_t)pidx * rows + row] * kLog2e;
+        if (pidx < kMergeStaged) sm_lse[pidx] = x;
+        m = fmaxf(m, x);
     }
-    sm_m[share][col] = m;
-    sm_l[share][col] = l;
-    sm_a[share][col] = a;
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) m = fmaxf(m, __shfl_xor(m, mask, 64));
+    if ((t & 63) == 0) sm_max[t >> 6] = m;
     __syncthreads();
-    if (share == 0) {
-        for (int g = 1; g < G; ++g) {
-            const float mg = sm_m[g][col];
-            if (mg == kNegInf) continue;
-            const float m_new = fmaxf(m, mg);
-            const float s0 = fast_exp2(m - m_new), s1 = fast_exp2(mg - m_new);
-            a = a * s0 + sm_a[g][col] * s1;
-            l = l * s0 + sm_l[g][col] * s1;
-            m = m_new;
+#pragma unroll
+    for (int i = 0; i < kMergeThreads / 64; ++i) m = fmaxf(m, sm_max[i]);
+    const float base = safe_base(m);
+
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float wsum = 0.0f;
+#pragma unroll 8
+    for (int pidx = lane; pidx < n_parts; pidx += LANES) {
+        const float lp = pidx < kMergeStaged ? sm_lse[pidx] : lse_parts[(int64_t)pidx * rows + row] * kLog2e;
+        const float w = fast_exp2(lp - base);  // 0 for an empty part (LSE = -inf)
+        const f32x4 x = *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)pidx * rows + row) * D + 4 * c);
+        if (w > 0.0f) acc += w * x;            // an empty part's output is never read into the sum
+        wsum += w;
+    }
+    sm_acc[lane][c] = acc;
+    if (c == 0) sm_w[lane] = wsum;
+    __syncthreads();
+    if (t < C) {
+        f32x4 a = sm_acc[0][t];
+        float l = sm_w[0];
+#pragma unroll
+        for (int i = 1; i < LANES; ++i) {
+            a += sm_acc[i][t];
+            l += sm_w[i];
         }
-        o[row * D + col] = (uint16_t)(pack_bf16x2(a / l, 0.0f) & 0xFFFFu);  // nearest even
-        if (col == 0) lse[row] = (m + fast_log2(l)) * kLn2;
+        const float inv = 1.0f / l;
+        u32x2 o2;
+        o2[0] = pack_bf16x2(a[0] * inv, a[1] * inv);  // nearest even
+        o2[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
+        *reinterpret_cast<u32x2*>(o + row * D + 4 * t) = o2;
+        if (t == 0) lse[row] = (m + fast_log2(l)) * kLn2;
     }
 }
 
-// Few rows (decoding a handful of streams): 1024 threads per row, so each walks fewer
-// parts; otherwise 256.
 template <int D>
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts,
                         int64_t rows, hipStream_t st) {
-    if (rows < 1024 && n_parts > 256 / D)
-        hipLaunchKernelGGL((attn_merge_kernel<D, 1024 / D>), dim3((unsigned)rows), dim3(1024), 0, st, o_parts,
-                           lse_parts, static_cast<uint16_t*>(o), lse, n_parts, rows);
-    else
-        hipLaunchKernelGGL((attn_merge_kernel<D, 256 / D>), dim3((unsigned)rows), dim3(256), 0, st, o_parts,
-                           lse_parts, static_cast<uint16_t*>(o), lse, n_parts, rows);
+    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)rows), dim3(kMergeThreads), 0, st, o_parts, lse_parts,
+                       static_cast<uint16_t*>(o), lse, n_parts, rows);
     return hipGetLastError();
 }
 
