@@ -322,26 +322,35 @@ def softmax_case(osm, workloads, torch, dev, name, inputs=None):
     return Case(name, run, bytes_, "GB/s", "hbm", PEAK_HBM_GBPS, "f32", nbytes(xd, yd), oracle), (xd, yd)
 
 
-def build_cases(osm, workloads, torch, dev, head, soft):
-    """Every workload and batch as a Case; head / soft are the step's own buffers."""
-    cases = []
-    # cfg 1: fp32 attention, every output
-    cases.append(attn_case(osm, workloads, torch, dev, "attn_f32_b1h1n256d64", None)[0])
-    # cfg 2: the step's softmax buffers, and the ragged 4095- and 1-column batches
-    cases.append(soft)
+def build_cases(osm, workloads, torch, dev, head, soft, want=None):
+    """Every workload and batch as a Case; head / soft are the step's own buffers.
+    want(name) -> bool, if given, limits the list (inputs are only made for those)."""
+    def attn(name, rows, **kw):
+        return lambda: attn_case(osm, workloads, torch, dev, name, rows, **kw)[0]
+
+    makers = [
+        # cfg 1: fp32 attention, every output
+        ("attn_f32_b1h1n256d64", attn("attn_f32_b1h1n256d64", None)),
+        # cfg 2: the step's softmax buffers, and the ragged 4095- and 1-column batches
+        (soft.name, lambda: soft),
+    ]
     for n in ("softmax_f32_65536x4095", "softmax_f32_65536x1"):
-        cases.append(softmax_case(osm, workloads, torch, dev, n)[0])
+        makers.append((n, lambda n=n: softmax_case(osm, workloads, torch, dev, n)[0]))
     # cfg 3, cfg 4 (the step's buffers), cfg 4' and cfg 5
-    cases.append(attn_case(osm, workloads, torch, dev, "attn_bf16_b4h16n2048d64", 32)[0])
-    cases.append(head)
-    cases.append(attn_case(osm, workloads, torch, dev, "attn_bf16_causal_b2h32n8191d128", 16)[0])
-    cases.append(attn_case(osm, workloads, torch, dev, "attn_bf16_causal_b1h8n131072d128", 64)[0])
-    # beyond the hot path: fp16 forward, gradients, split-KV decoding, fused norms
-    cases.append(attn_case(osm, workloads, torch, dev, ATTN, 16, fn_name="fa_fwd_f16", dtype_key="f16")[0])
-    cases.append(bwd_case(osm, workloads, torch, dev))
+    makers += [
+        ("attn_bf16_b4h16n2048d64", attn("attn_bf16_b4h16n2048d64", 32)),
+        (head.name, lambda: head),
+        ("attn_bf16_causal_b2h32n8191d128", attn("attn_bf16_causal_b2h32n8191d128", 16)),
+        ("attn_bf16_causal_b1h8n131072d128", attn("attn_bf16_causal_b1h8n131072d128", 64)),
+        # beyond the hot path: fp16 forward, gradients, split-KV decoding, fused norms
+        (ATTN.replace("bf16", "f16"), attn(ATTN, 16, fn_name="fa_fwd_f16", dtype_key="f16")),
+        ("attn_bwd_bf16_causal_b2h32n8192d128", lambda: bwd_case(osm, workloads, torch, dev)),
+    ]
     for n in ("decode_bf16_b1h8q1k131072d128", "decode_bf16_b4h32q16k32768d128"):
-        cases.append(decode_case(osm, workloads, torch, dev, n))
-    cases.extend(norm_cases(osm, workloads, torch, dev))
+        makers.append((n, lambda n=n: decode_case(osm, workloads, torch, dev, n)))
+    cases = [make() for name, make in makers if want is None or want(name)]
+    if want is None or any(want(p + "norm_bf16_16384x8192") for p in ("rmsnorm_", "layernorm_")):
+        cases.extend(c for c in norm_cases(osm, workloads, torch, dev) if want is None or want(c.name))
     return cases
 
 
@@ -564,6 +573,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload records")
     ap.add_argument("--only", choices=["attn", "softmax"], default=None,
                     help="time one kernel of the step only (for profiler runs; not the bench line)")
+    ap.add_argument("--records", metavar="SUBSTR", default=None,
+                    help="time only the per-workload records whose name contains SUBSTR and print them "
+                         "(for profiler runs; not the bench line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
@@ -608,6 +620,14 @@ def main():
     head, (qd, kd, vd, od, lsed) = attn_case(osm, workloads, torch, dev, ATTN, 16, inputs=(q, k, v))
     soft, (xd, yd) = softmax_case(osm, workloads, torch, dev, SOFTMAX, inputs=(x, x_sp))
     torch.cuda.synchronize()
+
+    if args.records is not None:
+        cases = build_cases(osm, workloads, torch, dev, head, soft, want=lambda n: args.records in n)
+        if not cases:
+            sys.exit(f"bench.py: no per-workload record matches {args.records!r}")
+        time_rounds(torch, cases, rounds=max(1, args.steps // 10) if args.steps else 3)
+        print(json.dumps({"records": {c.name: c.record() for c in cases}}))
+        return
 
     run_attn = args.only in (None, "attn")
     run_sm = args.only in (None, "softmax")
