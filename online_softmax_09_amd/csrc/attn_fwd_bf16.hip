@@ -55,6 +55,7 @@
 //     stream of a head is then shared through that XCD's L2.  In causal mode an XCD
 //     takes its heads in pairs and runs each pair's query tiles longest first across
 //     the pair.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -317,7 +318,11 @@ struct Wave {
     }
 };
 
-template <int D, bool CAUSAL, typename E, bool PP>
+// TAIL: the last key tile may run past N.  Causal kernels always take the general
+// form (their diagonal tile covers a ragged end anyway); non-causal ones are built
+// twice, and the form without key masks needs fewer registers (164 instead of 186 at
+// d = 64, so three blocks fit a CU instead of two).
+template <int D, bool CAUSAL, typename E, bool PP, bool TAIL>
 __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Params p) {
     constexpr int kBM = rows_of<PP>();
     using L = Layout<D>;
@@ -450,7 +455,7 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
     if (n_w > 0) w.qk(sa, k_lds0);
     __syncthreads();  // K buffer 0 may now be refilled
 
-    auto is_masked = [&](int j) { return (CAUSAL && j * kBN + kBN - 1 > qw0) || (j * kBN + kBN > N); };
+    auto is_masked = [&](int j) { return (CAUSAL && j * kBN + kBN - 1 > qw0) || (TAIL && j * kBN + kBN > N); };
     // In causal mode the only masked tile of a wavefront is its last, the diagonal tile
     // j = qw0 / 64, which starts 0 or 32 rows before the wavefront's rows.  Keys at or
     // past N on it lie above every stored row's diagonal, so the causal mask covers a
@@ -605,14 +610,49 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
     }
 }
 
-template <int D, bool CAUSAL, typename E, bool PP>
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Blocks of equal length (non-causal) run in rounds of `occ` per CU.  With three
+// 4-wavefront blocks per CU a CU does about 5% more work per unit time than with two,
+// and a lone block (one wavefront per SIMD) about 25% less; the last, partial round
+// decides which occupancy finishes first.  Returns true when two per CU is expected to
+// be faster for `per_cu` blocks on the busiest CU (for 4 blocks per CU: 4.0 against
+// 4.19 units; 7% faster measured at B=4 H=16 N=2048 d=64).
+bool two_per_cu_faster(int64_t per_cu) {
+    auto cost = [](int64_t n, int occ) {
+        constexpr double thr[4] = {0.0, 0.75, 1.0, 1.05};
+        return double(n / occ) * occ / thr[occ] + ((n % occ) ? double(n % occ) / thr[n % occ] : 0.0);
+    };
+    return cost(per_cu, 2) < cost(per_cu, 3);
+}
+
+template <int D, bool CAUSAL, typename E, bool PP, bool TAIL>
 hipError_t launch(Params p, hipStream_t st) {
     p.n_qtiles = (p.N + rows_of<PP>() - 1) / rows_of<PP>();
     const int64_t blocks = (int64_t)p.n_bh * p.n_qtiles;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     p.n_blocks = (int)blocks;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, E, PP>), dim3((unsigned)p.n_blocks),
-                       dim3(threads_of<PP>()), 0, st, p);
+    // d = 64 without key masks fits three blocks per CU by registers; unused dynamic
+    // LDS (4 K/V tiles of 8 KiB + 24 KiB = 56 KiB of the CU's 160 KiB) holds it to two
+    // when that finishes sooner.
+    unsigned lds_pad = 0;
+    if constexpr (D == 64 && !CAUSAL && !TAIL) {
+        const int cus = device_cus();
+        if (two_per_cu_faster((blocks + cus - 1) / cus)) lds_pad = 24 << 10;
+    }
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, E, PP, TAIL>), dim3((unsigned)p.n_blocks),
+                       dim3(threads_of<PP>()), lds_pad, st, p);
     return hipGetLastError();
 }
 
@@ -623,14 +663,20 @@ hipError_t launch(Params p, hipStream_t st) {
 // kernel's dispatch) the two met near causal N = 10240 (N / 128 key tiles per 256-row
 // block on average) and non-causal N = 4096, and the ping-pong led by 0.5-1.2% above;
 // at d = 64 the 4-wavefront form was faster at every length timed (2048 to 32768).
-template <int D, bool CAUSAL, typename E>
+template <int D, bool CAUSAL, typename E, bool TAIL>
 hipError_t launch_form(const Params& p, hipStream_t st) {
     if constexpr (D == 64) {
-        return launch<D, CAUSAL, E, false>(p, st);
+        return launch<D, CAUSAL, E, false, TAIL>(p, st);
     } else {
         const bool pp = CAUSAL ? p.N > 10240 : p.N > 4096;
-        return pp ? launch<D, CAUSAL, E, true>(p, st) : launch<D, CAUSAL, E, false>(p, st);
+        return pp ? launch<D, CAUSAL, E, true, TAIL>(p, st) : launch<D, CAUSAL, E, false, TAIL>(p, st);
     }
+}
+
+template <int D, typename E>
+hipError_t launch_mask(const Params& p, bool causal, hipStream_t st) {
+    if (causal) return launch_form<D, true, E, true>(p, st);
+    return p.N % kBN ? launch_form<D, false, E, true>(p, st) : launch_form<D, false, E, false>(p, st);
 }
 
 template <typename E>
@@ -650,8 +696,8 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, void* o, fl
     // 0 rather than 0 * -inf = NaN.
     p.scale_log2 = fmaxf(fabsf(scale) * kLog2e, 0x1p-100f);
     p.negate_q = scale < 0.0f;  // flipping the sign bit negates exactly in bf16 and in fp16
-    if (d == 64) return causal ? launch_form<64, true, E>(p, st) : launch_form<64, false, E>(p, st);
-    if (d == 128) return causal ? launch_form<128, true, E>(p, st) : launch_form<128, false, E>(p, st);
+    if (d == 64) return launch_mask<64, E>(p, causal, st);
+    if (d == 128) return launch_mask<128, E>(p, causal, st);
     return hipErrorInvalidValue;
 }
 

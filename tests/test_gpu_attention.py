@@ -318,3 +318,27 @@ def test_both_block_forms(N, causal, fn, dtype, tol_o, tol_l):
     assert eo <= tol_o and el <= tol_l
     if causal:
         assert np.array_equal(o[:, :, 0], v[:, :, 0].float().numpy())
+
+
+@pytest.mark.parametrize("B,H,N,d", [(4, 16, 4096, 64), (4, 16, 4100, 64), (1, 2, 8192, 128), (1, 2, 8200, 128),
+                                     (1, 2, 2048, 128)])
+def test_non_causal_key_tail_forms(B, H, N, d):
+    """Non-causal kernels are built twice: with key masks for a last key tile that runs
+    past N (N not a multiple of 64) and without them.  At d = 64 the build without masks
+    fits three blocks per CU, and the host holds it to two for grids of four blocks per
+    CU (the full B=4 H=16 N=2048 workload covers that case); 2048 blocks here run three
+    per CU.  At d = 128 both builds are taken in both block forms (N = 2048 plain,
+    N = 8192 ping-pong).  Sampled rows include both ends and tile edges."""
+    dev = need_gpu()
+    q, k, v = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 7500 + N + d)
+    scale = workloads.default_scale(d)
+    rows = workloads.sampled_query_rows(B, H, N, 48, seed=workloads.SEED_BASE + 7500 + N)
+    edges = np.array([r for r in TILE_EDGES + (N - 2, N - 1) if r < N], dtype=np.int64)
+    rows = np.concatenate([rows, np.broadcast_to(edges, (B, H, len(edges)))], axis=2)
+    say(f"case bf16 non-causal key tail B={B} H={H} N={N} d={d}")
+    o, lse = _gpu(osm.fa_fwd, q, k, v, scale, False, dev)
+    o_ref, lse_ref = oracle_rows_per_head(q, k, v, scale, False, rows)
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, :, None]
+    eo, el = _report("bf16", o[bi, hi, rows], lse[bi, hi, rows], o_ref, lse_ref, 1e-3)
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
