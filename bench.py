@@ -17,7 +17,8 @@ Prints ONE JSON line:
              the dispatch time, from a committed rocprofv3 counter run of the same source)
              and the attention throughput against the matrix-core peak at that clock
   configs    every workload and batch, one record each: latency (mean, median, min, max of
-             launches timed in interleaved rounds after their own warm-up), throughput, the
+             the per-launch times of batches of back-to-back launches, timed in interleaved
+             rounds after their own warm-up), throughput, the
              fraction of its roofline, the device bytes the call touches (the library
              allocates nothing) and, from the cpu_baseline leg, the max abs and max rel
              error against the float64 oracle on sampled outputs
@@ -213,14 +214,16 @@ class Case:
         self.bound, self.peak, self.dtype, self.device_bytes = bound, peak, dtype, device_bytes
         self.oracle = oracle  # callable(oracle module) -> error record, run in the cpu_baseline leg
         self.note = note
-        self.ms = []
+        self.ms = []  # per-launch time of each timed batch
+        self.launches = 0
 
     def record(self):
         ms = np.array(self.ms)
         mean = float(ms.mean())
         thr = self.work / (mean * 1e-3) / (1e12 if self.unit == "TFLOP/s" else 1e9)
         rec = {"dtype": self.dtype, "ms_mean": round(mean, 4), "ms_median": round(float(np.median(ms)), 4),
-               "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4), "launches": len(ms),
+               "ms_min": round(float(ms.min()), 4), "ms_max": round(float(ms.max()), 4), "batches": len(ms),
+               "launches": self.launches,
                "work_per_launch": self.work, "throughput": round(thr, 2), "unit": self.unit,
                "roofline": {"bound": self.bound, "peak": self.peak,
                             "frac": round(thr / self.peak, 4) if self.peak else None},
@@ -466,10 +469,12 @@ def norm_cases(osm, workloads, torch, dev):
     return out
 
 
-def time_rounds(torch, cases, rounds=3, target_s=0.04):
+def time_rounds(torch, cases, rounds=3, target_s=0.04, batches=4):
     """Time every case in interleaved rounds: in each round each case gets a short
-    warm-up and then a batch of launches, each bracketed by HIP events, so that all
-    cases see the same mix of clock and thermal states."""
+    warm-up and then `batches` batches of back-to-back launches, each batch between
+    two HIP events, so that all cases see the same mix of clock and thermal states.
+    A sample is one batch's time per launch (short kernels are not charged for an
+    event between every two launches)."""
     est = {}
     for cs in cases:  # first call: compile-free, but caches and clocks settle
         cs.run()
@@ -482,16 +487,19 @@ def time_rounds(torch, cases, rounds=3, target_s=0.04):
         est[cs.name] = max(e0.elapsed_time(e1) * 1e-3, 1e-6)
     for _ in range(rounds):
         for cs in cases:
-            n = int(min(50, max(3, target_s / est[cs.name])))
+            n = int(min(48, max(batches, target_s / est[cs.name])))
+            per = max(1, n // batches)
             for _ in range(max(2, n // 4)):
                 cs.run()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(batches)]
             for a, b in evs:
                 a.record()
-                cs.run()
+                for _ in range(per):
+                    cs.run()
                 b.record()
             torch.cuda.synchronize()
-            cs.ms.extend(a.elapsed_time(b) for a, b in evs)
+            cs.ms.extend(a.elapsed_time(b) / per for a, b in evs)
+            cs.launches += per * batches
 
 
 def cpu_baseline_leg(q, k, v, scale, causal, o_gpu, lse_gpu, budget_s, cases):
@@ -760,7 +768,9 @@ def main():
         "configs": configs,
         "flushed": flushed,
         "timing": {"method": "HIP events on the launch stream", "l2_flush": False,
-                   "configs": "3 interleaved rounds, each case warmed before its launches",
+                   "configs": "3 interleaved rounds; per case and round a warm-up, then 4 batches of "
+                              "back-to-back launches, each batch between two HIP events "
+                              "(ms_* are per-launch times of the batches)",
                    "wall_s_timed_region": round(wall, 3), "input_gen_s": round(t_gen, 1),
                    "device_peak_allocated_bytes": int(torch.cuda.max_memory_allocated(dev))},
         "inputs_sha256_16": hashes,

@@ -179,6 +179,10 @@ int64_t fa_bwd_workspace_bytes(int B, int H, int N);
  *              trailing parts may be empty.
  *   d, scale, stream  as for fa_fwd.
  * o, lse and workspace must not overlap each other or any input.
+ * Arithmetic: with Nq > 1 the products run on bf16 matrix cores with float32 accumulation
+ * and P rounded to bf16, as in fa_fwd; with Nq = 1 (one query per head) the scores and the
+ * P V sums are float32 multiply-adds of the bf16 inputs, P not rounded.  The partial results
+ * are float32; o is rounded once at the end of the merge.
  */
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
                    int B, int H, int Nq, int Nk, int d, float scale, int causal, int n_splits, void* stream);

@@ -21,10 +21,14 @@
 // by the transposing LDS load.  The running maximum follows the pages' rule exactly
 // (moved at every sub-tile); O is rescaled only when some row's maximum moved.
 //
+// One-query kernel: with a single query the part is a matrix-vector product, so it
+// reads K and V rows straight into registers and reduces the dot products with DPP
+// (no matrix cores, no LDS staging; see attn_decode_partial_kernel).
+//
 // Merge kernel: one block of 256 threads per query row; threads own a 16-byte chunk of
-// the output columns and a lane of the parts.  The row's LSEs are read once (and staged
-// in LDS) for the maximum, then every part's output chunk is summed with the weight
-// e^{LSE_p - max} (independent loads, unrolled), and the lanes' sums add up through LDS.
+// the output columns and a lane of the parts.  Each lane loads its parts' LSEs and
+// output chunks in one round of independent loads and keeps a running (m, l, O) state;
+// the lanes' states then merge through LDS with the same rescaling rule.
 #include <mutex>
 
 #include "device_common.hpp"
@@ -259,77 +263,242 @@ __global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams
 }
 
 // ---------------------------------------------------------------------------------
-// Merge: one block of 256 threads per row.  Thread t owns the 16-byte column chunk
-// c = t % (D / 4) of part lane t / (D / 4) (parts lane, lane + lanes, ...).  Two rounds of
-// independent loads: every part's LSE (staged in LDS as LSE log2 e), the block maximum,
-// then every part's output chunk weighted by e^{LSE_p - max}; the lanes' sums then add
-// up through LDS.  All weights share the block maximum, so no lane rescales another.
+// One query (decoding one token per head): the part is a matrix-vector product over
+// the key/value cache with no matrix-core work, so it skips the 32-query MFMA tile and
+// the LDS staging.  Lane l of a wavefront reads the 16-byte column chunk l % CH of key
+// row l / CH (CH = D / 8 lanes per row), and each wavefront loads U such rows of K and
+// of V per iteration straight into registers (U * 2 KiB in flight per wavefront; with
+// several blocks per CU that keeps HBM busy without any LDS).  A score is the lane's
+// 8-term partial dot product summed over the row's CH lanes with DPP; the online-softmax
+// state (m, l, O chunk) is per lane and exact (m moves whenever a score exceeds it), and
+// the states of the block's key rows merge through LDS with the same rule at the end.
 // ---------------------------------------------------------------------------------
-constexpr int kMergeThreads = 256;
-constexpr int kMergeStaged = 2048;  // parts whose LSE stays in LDS between the passes
+constexpr int kGvThreads = 256;
+constexpr int kGvU = 8;  // key rows per lane and iteration
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// x + (x of lane `ctrl` points to), with every lane taking part.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
+                                                                     false));
+}
+
+// Sum over aligned groups of CH lanes (CH = 16: a DPP row; CH = 8: half a row), left
+// in every lane of the group.
+template <int CH>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (CH == 16) {
+        x = dpp_add<0x128>(x);  // row_ror:8
+        x = dpp_add<0x124>(x);  // row_ror:4
+    } else {
+        x = dpp_add<0x141>(x);  // row_half_mirror
+    }
+    x = dpp_add<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+    x = dpp_add<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+    return x;
+}
 
 template <int D>
+__global__ __launch_bounds__(kGvThreads) void attn_decode_partial_kernel(SplitParams p) {
+    constexpr int CH = D / 8;                    // lanes per key row
+    constexpr int KPW = 64 / CH;                 // key rows per wavefront load
+    constexpr int WAVES = kGvThreads / 64;
+    constexpr int KPI = WAVES * kGvU * KPW;      // keys per block iteration
+    constexpr int R = WAVES * KPW;               // states merged at the end, per chunk
+    __shared__ float sm_m[R][CH];
+    __shared__ float sm_l[R][CH];
+    __shared__ f32x4 sm_acc[R][CH][2];
+
+    const int64_t bid = blockIdx.x;
+    const int s = (int)(bid % p.n_parts);
+    const int64_t bh = bid / p.n_parts;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int c = lane % CH, kr = lane / CH;
+    const int Nk = p.Nk;
+    const int lo = (int)min((int64_t)Nk, (int64_t)s * p.chunk);
+    const int hi = (int)min((int64_t)Nk, (int64_t)lo + p.chunk);
+
+    // the query's chunk, with the sign of the scale folded in (exact)
+    float qf[8];
+    {
+        const u32x4 qw = *reinterpret_cast<const u32x4*>(p.q + bh * D + 8 * c);
+        const float sg = p.negate_q ? -1.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            qf[2 * j] = sg * bf16_lo(qw[j]);
+            qf[2 * j + 1] = sg * bf16_hi(qw[j]);
+        }
+    }
+    const uint16_t* kh = p.k + bh * (int64_t)Nk * D + 8 * c;
+    const uint16_t* vh = p.v + bh * (int64_t)Nk * D + 8 * c;
+
+    float m = kNegInf, l = 0.0f;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = lo; kb < hi; kb += KPI) {
+        const int k0 = kb + wave * kGvU * KPW + kr;  // this lane's first key row
+        u32x4 kv[kGvU], vv[kGvU];
+#pragma unroll
+        for (int u = 0; u < kGvU; ++u) {
+            const int key = min(k0 + u * KPW, hi - 1);  // rows past the part load its last row, masked below
+            kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kh + (int64_t)key * D));
+        }
+#pragma unroll
+        for (int u = 0; u < kGvU; ++u) {
+            const int key = min(k0 + u * KPW, hi - 1);
+            vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vh + (int64_t)key * D));
+        }
+        float sc[kGvU];
+        float mx = kNegInf;
+#pragma unroll
+        for (int u = 0; u < kGvU; ++u) {
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                d0 = fmaf(qf[2 * j], bf16_lo(kv[u][j]), d0);
+                d1 = fmaf(qf[2 * j + 1], bf16_hi(kv[u][j]), d1);
+            }
+            const float dot = group_sum<CH>(d0 + d1);
+            sc[u] = k0 + u * KPW < hi ? dot * p.c : kNegInf;
+            mx = fmaxf(mx, sc[u]);
+        }
+        const float m_new = fmaxf(m, mx);
+        const float base = safe_base(m_new);
+        const float alpha = fast_exp2(m - base);  // 0 while m = -inf
+        l *= alpha;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+#pragma unroll
+        for (int u = 0; u < kGvU; ++u) {
+            const float e = fast_exp2(sc[u] - base);  // 0 for a masked row
+            l += e;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[2 * j] = fmaf(e, bf16_lo(vv[u][j]), acc[2 * j]);
+                acc[2 * j + 1] = fmaf(e, bf16_hi(vv[u][j]), acc[2 * j + 1]);
+            }
+        }
+        m = m_new;
+    }
+
+    const int r = wave * KPW + kr;
+    sm_m[r][c] = m;
+    sm_l[r][c] = l;
+    sm_acc[r][c][0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    sm_acc[r][c][1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    __syncthreads();
+    if (t < D) {
+        const int cc = t / 8, i = t % 8;
+        float M = kNegInf;
+#pragma unroll
+        for (int q = 0; q < R; ++q) M = fmaxf(M, sm_m[q][cc]);
+        const float base = safe_base(M);
+        float a = 0.0f, L = 0.0f;
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+            const float w = fast_exp2(sm_m[q][cc] - base);
+            a = fmaf(w, sm_acc[q][cc][i / 4][i % 4], a);
+            L = fmaf(w, sm_l[q][cc], L);
+        }
+        const bool empty = !(L > 0.0f);
+        p.o_part[((int64_t)s * p.rows + bh) * D + t] = empty ? 0.0f : a / L;
+        if (t == 0) p.lse_part[(int64_t)s * p.rows + bh] = empty ? kNegInf : (M + fast_log2(L)) * kLn2;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Merge: one block of 256 threads per row.  Thread t owns the 16-byte column chunk
+// c = t % (D / 4) of part lane t / (D / 4) (parts lane, lane + lanes, ...).  A lane
+// loads the LSEs and output chunks of up to BATCH parts at once (with BATCH = 16 one
+// round of independent loads covers 128 parts at d = 128 and 256 at d = 64; few parts
+// take BATCH = 4, whose smaller register count lets more rows run at once), folds them
+// into its own state (m, l, O chunk) with the online rescaling rule, and the lanes'
+// states merge through LDS with the same rule.
+// ---------------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+
+template <int D, int BATCH>
 __global__ __launch_bounds__(kMergeThreads) void attn_merge_kernel(const float* o_parts, const float* lse_parts,
                                                                    uint16_t* o, float* lse, int n_parts,
                                                                    int64_t rows) {
     constexpr int C = D / 4;                  // 16-byte chunks per row
     constexpr int LANES = kMergeThreads / C;  // part lanes
-    __shared__ float sm_lse[kMergeStaged];
-    __shared__ float sm_max[kMergeThreads / 64];
     __shared__ f32x4 sm_acc[LANES][C];
-    __shared__ float sm_w[LANES];
+    __shared__ float sm_m[LANES];
+    __shared__ float sm_l[LANES];
     const int64_t row = blockIdx.x;
     const int t = threadIdx.x, c = t % C, lane = t / C;
 
-    float m = kNegInf;
-    for (int pidx = t; pidx < n_parts; pidx += kMergeThreads) {
-        const float x = lse_parts[(int64_t)pidx * rows + row] * kLog2e;
-        if (pidx < kMergeStaged) sm_lse[pidx] = x;
-        m = fmaxf(m, x);
-    }
-#pragma unroll
-    for (int mask = 32; mask >= 1; mask >>= 1) m = fmaxf(m, __shfl_xor(m, mask, 64));
-    if ((t & 63) == 0) sm_max[t >> 6] = m;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kMergeThreads / 64; ++i) m = fmaxf(m, sm_max[i]);
-    const float base = safe_base(m);
-
+    float m = kNegInf, l = 0.0f;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    float wsum = 0.0f;
-#pragma unroll 8
-    for (int pidx = lane; pidx < n_parts; pidx += LANES) {
-        const float lp = pidx < kMergeStaged ? sm_lse[pidx] : lse_parts[(int64_t)pidx * rows + row] * kLog2e;
-        const float w = fast_exp2(lp - base);  // 0 for an empty part (LSE = -inf)
-        const f32x4 x = *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)pidx * rows + row) * D + 4 * c);
-        if (w > 0.0f) acc += w * x;            // an empty part's output is never read into the sum
-        wsum += w;
+    for (int p0 = lane; p0 < n_parts; p0 += BATCH * LANES) {
+        float lp[BATCH];
+        f32x4 x[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int pidx = p0 + b * LANES;
+            lp[b] = kNegInf;
+            x[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (pidx < n_parts) {
+                lp[b] = lse_parts[(int64_t)pidx * rows + row] * kLog2e;
+                x[b] = *reinterpret_cast<const f32x4*>(o_parts + ((int64_t)pidx * rows + row) * D + 4 * c);
+            }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) mx = fmaxf(mx, lp[b]);
+        const float m_new = fmaxf(m, mx);
+        const float base = safe_base(m_new);
+        const float alpha = fast_exp2(m - base);  // 0 while m = -inf
+        acc *= alpha;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const float w = fast_exp2(lp[b] - base);  // 0 for an empty part (LSE = -inf)
+            if (w > 0.0f) acc += w * x[b];            // an empty part's output is never read into the sum
+            l += w;
+        }
+        m = m_new;
     }
     sm_acc[lane][c] = acc;
-    if (c == 0) sm_w[lane] = wsum;
+    if (c == 0) {
+        sm_m[lane] = m;
+        sm_l[lane] = l;
+    }
     __syncthreads();
     if (t < C) {
-        f32x4 a = sm_acc[0][t];
-        float l = sm_w[0];
+        float M = kNegInf;
 #pragma unroll
-        for (int i = 1; i < LANES; ++i) {
-            a += sm_acc[i][t];
-            l += sm_w[i];
+        for (int i = 0; i < LANES; ++i) M = fmaxf(M, sm_m[i]);
+        const float base = safe_base(M);
+        f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+        float L = 0.0f;
+#pragma unroll
+        for (int i = 0; i < LANES; ++i) {
+            const float w = fast_exp2(sm_m[i] - base);
+            a += w * sm_acc[i][t];
+            L += w * sm_l[i];
         }
-        const float inv = 1.0f / l;
+        const float inv = 1.0f / L;
         u32x2 o2;
         o2[0] = pack_bf16x2(a[0] * inv, a[1] * inv);  // nearest even
         o2[1] = pack_bf16x2(a[2] * inv, a[3] * inv);
         *reinterpret_cast<u32x2*>(o + row * D + 4 * t) = o2;
-        if (t == 0) lse[row] = (m + fast_log2(l)) * kLn2;
+        if (t == 0) lse[row] = (M + fast_log2(L)) * kLn2;
     }
 }
 
 template <int D>
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, void* o, float* lse, int n_parts,
                         int64_t rows, hipStream_t st) {
-    hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)rows), dim3(kMergeThreads), 0, st, o_parts, lse_parts,
-                       static_cast<uint16_t*>(o), lse, n_parts, rows);
+    if (n_parts <= 4 * (kMergeThreads / (D / 4)))
+        hipLaunchKernelGGL((attn_merge_kernel<D, 4>), dim3((unsigned)rows), dim3(kMergeThreads), 0, st, o_parts,
+                           lse_parts, static_cast<uint16_t*>(o), lse, n_parts, rows);
+    else
+        hipLaunchKernelGGL((attn_merge_kernel<D, 16>), dim3((unsigned)rows), dim3(kMergeThreads), 0, st, o_parts,
+                           lse_parts, static_cast<uint16_t*>(o), lse, n_parts, rows);
     return hipGetLastError();
 }
 
@@ -367,7 +536,14 @@ hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v,
     p.negate_q = scale < 0.0f;
     const int64_t blocks = (int64_t)B * H * p.n_qt * n_parts;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (d == 64) {
+    if (Nq == 1) {  // one query sees every key, causal or not
+        if (d == 64)
+            hipLaunchKernelGGL((attn_decode_partial_kernel<64>), dim3((unsigned)blocks), dim3(kGvThreads), 0, st, p);
+        else if (d == 128)
+            hipLaunchKernelGGL((attn_decode_partial_kernel<128>), dim3((unsigned)blocks), dim3(kGvThreads), 0, st, p);
+        else
+            return hipErrorInvalidValue;
+    } else if (d == 64) {
         if (causal)
             hipLaunchKernelGGL((attn_splitkv_partial_kernel<64, true>), dim3((unsigned)blocks), dim3(64), 0, st, p);
         else

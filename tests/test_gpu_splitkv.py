@@ -30,7 +30,8 @@ def _gpu_splitkv(q, k, v, scale, causal, n_splits, dev):
     (1, 2, 1, 1000, 128, True, 4), (1, 2, 1, 1000, 128, False, 1), (2, 3, 5, 777, 64, True, 7),
     (1, 1, 32, 4096, 128, True, 16), (1, 2, 40, 300, 64, False, 3), (1, 1, 1, 1, 64, True, 1),
     (1, 1, 3, 3, 128, True, 2), (1, 1, 1, 64, 128, True, 8), (1, 1, 7, 100, 64, True, 4096),
-    (2, 2, 16, 2049, 128, True, 32), (1, 1, 33, 33, 128, True, 3), (1, 2, 70, 50, 128, False, 2)])
+    (2, 2, 16, 2049, 128, True, 32), (1, 1, 33, 33, 128, True, 3), (1, 2, 70, 50, 128, False, 2),
+    (1, 3, 1, 4999, 64, False, 5), (2, 2, 1, 3000, 128, True, 40), (1, 1, 1, 300, 64, True, 64)])
 def test_splitkv_shapes(B, H, Nq, Nk, d, causal, n_splits):
     dev = need_gpu()
     say(f"case splitkv B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal} n_splits={n_splits}")
@@ -104,11 +105,13 @@ def test_splitkv_deterministic():
 
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("B,H,Nq,Nk,d,n_splits", [(1, 2, 3, 1000, 128, 4), (1, 1, 5, 300, 64, 16)])
+@pytest.mark.parametrize("B,H,Nq,Nk,d,n_splits", [(1, 2, 3, 1000, 128, 4), (1, 1, 5, 300, 64, 16),
+                                                  (1, 2, 1, 1000, 64, 4), (1, 1, 1, 2000, 128, 3)])
 def test_splitkv_scales(scale, causal, B, H, Nq, Nk, d, n_splits):
-    """The partial kernel's own scale handling (negated Q for a negative scale, c = |scale|
+    """The partial kernels' own scale handling (negated Q for a negative scale, c = |scale|
     log2 e) at scale 0 (uniform weights over the visible keys), a negative scale and a
-    large one.  n_splits = 16 over 300 keys leaves trailing parts empty."""
+    large one, for the multi-query kernel and the one-query kernel.  n_splits = 16 over
+    300 keys leaves trailing parts empty."""
     dev = need_gpu()
     say(f"case splitkv scale={scale} causal={causal} B={B} H={H} Nq={Nq} Nk={Nk} d={d} n_splits={n_splits}")
     q, k, v = workloads.decode_inputs(B, H, Nq, Nk, d, seed=workloads.SEED_BASE + 8400 + Nk + d)
@@ -150,13 +153,15 @@ def test_merge_states_of_partials_at_scales(scale):
     assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
 
 
+@pytest.mark.parametrize("Nq", [5, 1])
 @pytest.mark.parametrize("causal", [True, False])
-def test_splitkv_partials_follow_the_part_contract(causal):
+def test_splitkv_partials_follow_the_part_contract(causal, Nq):
     """The workspace after a call holds each part's normalised output and LSE over exactly
     the keys [lo, hi) the header states (64-key multiples), with (0, -inf) for a row that
-    sees no key of its part."""
+    sees no key of its part (multi-query and one-query kernels)."""
     dev = need_gpu()
-    B, H, Nq, Nk, d, n = 1, 2, 5, 1000, 128, 6
+    B, H, Nk, d = 1, 2, 1000, 128
+    n = 6 if Nq > 1 else 24  # one query: 64-key parts, the last eight empty
     say(f"case splitkv partials causal={causal} B={B} H={H} Nq={Nq} Nk={Nk} d={d} n_splits={n}")
     q, k, v = workloads.decode_inputs(B, H, Nq, Nk, d, seed=workloads.SEED_BASE + 8600)
     scale = workloads.default_scale(d)
