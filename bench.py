@@ -571,6 +571,18 @@ def time_flushed(torch, run, calls, flush):
     return round(float(np.mean(ms)), 4)
 
 
+def calib_copy(torch, dev, mib):
+    """Two plain device copies of `mib` MiB: the known byte count that calibrates the HBM
+    byte counters of a profiler run."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -634,6 +646,8 @@ def main():
         if not cases:
             sys.exit(f"bench.py: no per-workload record matches {args.records!r}")
         time_rounds(torch, cases, rounds=max(1, args.steps // 10) if args.steps else 3)
+        if args.calib_copy_mib:
+            calib_copy(torch, dev, args.calib_copy_mib)
         print(json.dumps({"records": {c.name: c.record() for c in cases}}))
         return
 
@@ -674,13 +688,7 @@ def main():
     sm_ms = [e[2].elapsed_time(e[3]) for e in evs] if run_sm else []
 
     if args.calib_copy_mib:
-        n = args.calib_copy_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calib_copy(torch, dev, args.calib_copy_mib)
 
     fl = attn_flops(B, H, N, d, causal)
     attn_min_bytes = 2.0 * B * H * N * d * 4 + 4.0 * B * H * N  # read Q, K, V; write O; write LSE
