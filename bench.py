@@ -593,9 +593,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload records")
     ap.add_argument("--only", choices=["attn", "softmax"], default=None,
                     help="time one kernel of the step only (for profiler runs; not the bench line)")
-    ap.add_argument("--records", metavar="SUBSTR", default=None,
-                    help="time only the per-workload records whose name contains SUBSTR and print them "
-                         "(for profiler runs; not the bench line)")
+    ap.add_argument("--records", metavar="SUBSTR[,SUBSTR...]", default=None,
+                    help="time only the per-workload records whose name contains one of the given "
+                         "substrings and print them (for profiler runs; not the bench line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
@@ -642,7 +642,8 @@ def main():
     torch.cuda.synchronize()
 
     if args.records is not None:
-        cases = build_cases(osm, workloads, torch, dev, head, soft, want=lambda n: args.records in n)
+        subs = [x for x in args.records.split(",") if x]
+        cases = build_cases(osm, workloads, torch, dev, head, soft, want=lambda n: any(x in n for x in subs))
         if not cases:
             sys.exit(f"bench.py: no per-workload record matches {args.records!r}")
         time_rounds(torch, cases, rounds=max(1, args.steps // 10) if args.steps else 3)
