@@ -342,3 +342,22 @@ def test_non_causal_key_tail_forms(B, H, N, d):
     hi = np.arange(H)[None, :, None]
     eo, el = _report("bf16", o[bi, hi, rows], lse[bi, hi, rows], o_ref, lse_ref, 1e-3)
     assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+
+
+@pytest.mark.parametrize("B,H,N", [(2, 8, 2048), (1, 8, 1024), (1, 16, 4096)])
+def test_causal_d64_dispatch_order(B, H, N):
+    """Causal d = 64 launches whose blocks divide evenly over the 8 XCDs take a dispatch
+    order that holds back the shortest quarter of every head's query tiles (one head per
+    XCD, pairs of heads, two pairs).  Every output row is compared, so a tile computed
+    twice or never shows up."""
+    dev = need_gpu()
+    d = 64
+    q, k, v = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 7600 + N + H)
+    scale = workloads.default_scale(d)
+    say(f"case bf16 causal d=64 dispatch order B={B} H={H} N={N}")
+    o, lse = _gpu(osm.fa_fwd, q, k, v, scale, True, dev)
+    rows = np.broadcast_to(np.arange(N), (B, H, N))
+    o_ref, lse_ref = oracle_rows_per_head(q, k, v, scale, True, rows)
+    eo, el = _report("bf16", o, lse, o_ref, lse_ref, 1e-3)
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    assert np.array_equal(o[:, :, 0], v[:, :, 0].float().numpy())
