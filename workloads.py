@@ -214,6 +214,24 @@ def scalar_rows(seed=SEED_BASE + 0, per_length=10, max_length=39):
     return rows
 
 
+def device_normal(shape, seed, dtype, device, chunk=1 << 27):
+    """A tensor of ``shape`` on ``device`` filled with iid N(0, 1) values from torch's
+    seeded generator on that device, rounded to ``dtype`` (a torch dtype), drawn in
+    chunks so that no float32 copy of the whole tensor is made.  For inputs too large to
+    draw on the host (more than 2^31 elements); the same seed and device give the same
+    values."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    for s0 in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - s0)
+        flat[s0:s0 + n] = torch.randn(n, generator=g, device=device, dtype=torch.float32).to(dtype)
+    return out
+
+
 def sampled_query_rows(B, H, N, per_head, seed):
     """int64 [B, H, per_head + 2]: distinct rows from 1..N-2 per head, plus 0 and N-1."""
     g = generator(seed + 7)
