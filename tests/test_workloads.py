@@ -61,3 +61,22 @@ def test_sampled_rows():
 def test_default_scale():
     assert workloads.default_scale(64) == 0.125
     assert math.isclose(workloads.default_scale(128), 1 / math.sqrt(128), rel_tol=1e-7)
+
+
+def test_device_normal_is_seeded_and_chunked():
+    """The device-side generator of the very large inputs: the same seed and chunk size
+    give the same values (the chunk size is part of the recipe: drawing in pieces gives
+    other values than one draw), and the values are the generator's N(0, 1) draws rounded
+    once to the requested type.  Checked on the host device."""
+    import torch
+
+    a = workloads.device_normal((7, 13), 1234, torch.float32, "cpu")
+    b = workloads.device_normal((7, 13), 1234, torch.float32, "cpu", chunk=10)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1234)
+    ref = torch.randn(91, generator=g, dtype=torch.float32).view(7, 13)
+    assert torch.equal(a, ref)
+    assert not torch.equal(b, ref)  # chunked draws continue the same stream in pieces
+    c = workloads.device_normal((7, 13), 1234, torch.bfloat16, "cpu")
+    assert torch.equal(c, ref.to(torch.bfloat16))
+    assert not torch.equal(a, workloads.device_normal((7, 13), 1235, torch.float32, "cpu"))

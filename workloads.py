@@ -218,8 +218,8 @@ def device_normal(shape, seed, dtype, device, chunk=1 << 27):
     """A tensor of ``shape`` on ``device`` filled with iid N(0, 1) values from torch's
     seeded generator on that device, rounded to ``dtype`` (a torch dtype), drawn in
     chunks so that no float32 copy of the whole tensor is made.  For inputs too large to
-    draw on the host (more than 2^31 elements); the same seed and device give the same
-    values."""
+    draw on the host (more than 2^31 elements); the same seed, device and chunk size give
+    the same values."""
     import torch
 
     g = torch.Generator(device=device)
