@@ -13,8 +13,9 @@
 //   * Each wavefront owns 32 query rows for the whole key loop; key tiles are 64 keys.
 //     Two block forms share the code.  The ping-pong form has 8 wavefronts (256
 //     query rows; waves w and w + 4 share a SIMD) and one block per CU.  The plain
-//     form has 4 wavefronts (128 rows) and two blocks per CU.  The host picks one per
-//     shape (launch_form).
+//     form has 4 wavefronts (128 rows) and two blocks per CU (three at d = 64 when the
+//     kernel needs no key masks, unless the host holds it to two, see launch).  The
+//     host picks one per shape (launch_form).
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     A = a 32-key slice of K (from LDS), B = Q^T (held in registers for the whole
 //     loop).  In the 32x32 accumulator, lane l holds one column, i.e. one query row
@@ -54,7 +55,7 @@
 //     robin) walks a contiguous range of (head, query tile) pairs: the key/value
 //     stream of a head is then shared through that XCD's L2.  In causal mode an XCD
 //     takes its heads in pairs and runs each pair's query tiles longest first across
-//     the pair.
+//     the pair (at d = 64 the shortest quarter of every head's tiles comes last).
 #include <atomic>
 #include <type_traits>
 

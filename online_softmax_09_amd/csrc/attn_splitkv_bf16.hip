@@ -267,14 +267,18 @@ __global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams
 // the key/value cache with no matrix-core work, so it skips the 32-query MFMA tile and
 // the LDS staging.  Lane l of a wavefront reads the 16-byte column chunk l % CH of key
 // row l / CH (CH = D / 8 lanes per row), and each wavefront loads U such rows of K and
-// of V per iteration straight into registers (U * 2 KiB in flight per wavefront; with
-// several blocks per CU that keeps HBM busy without any LDS).  A score is the lane's
+// of V per iteration straight into registers (U * 2 KiB in flight per wavefront; with a
+// block on every CU that keeps HBM busy without any LDS).  A score is the lane's
 // 8-term partial dot product summed over the row's CH lanes with DPP; the online-softmax
 // state (m, l, O chunk) is per lane and exact (m moves whenever a score exceeds it), and
 // the states of the block's key rows merge through LDS with the same rule at the end.
 // ---------------------------------------------------------------------------------
 constexpr int kGvThreads = 256;
-constexpr int kGvU = 8;  // key rows per lane and iteration
+// Key rows per lane and iteration.  Timed at 8 heads x 131072 keys (GB/s, one box): 4 rows
+// with one block per CU (32 parts) 6856; 8 rows 6454 there and 6733 with 24 parts (192
+// blocks); 2 and 6 rows lower; plain instead of non-temporal loads 5669.  Eight rows win
+// only when the grid leaves CUs idle.
+constexpr int kGvU = 4;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

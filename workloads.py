@@ -53,7 +53,7 @@ CONFIGS = {
     # Decoding against a key/value cache: the long causal workload's heads with one new
     # query each (bottom-right aligned), keys cut into parts merged in the log domain.
     "decode_bf16_b1h8q1k131072d128": dict(kind="decode", dtype="bf16", B=1, H=8, Nq=1, Nk=131072,
-                                          d=128, causal=True, n_splits=24, seed=SEED_BASE + 5),
+                                          d=128, causal=True, n_splits=32, seed=SEED_BASE + 5),
     # A batch of decoding streams with 16 queries each (speculative or chunked decoding).
     "decode_bf16_b4h32q16k32768d128": dict(kind="decode", dtype="bf16", B=4, H=32, Nq=16, Nk=32768,
                                            d=128, causal=True, n_splits=16, seed=SEED_BASE + 6),
