@@ -4,8 +4,9 @@ caller-supplied workspace on the same inputs.
 
 Both run the same kernels in the same order, so the outputs must agree bit for bit; they
 are also held to the bf16 gates against the float64 oracle (O max abs <= 2e-2, LSE max
-abs <= 1e-2).  Two calls run in a row, the second smaller than the first, so the second
-reads a scratch that still holds the first call's partials.
+abs <= 1e-2).  Three calls run in a row, each smaller than the one before, so each reads a
+scratch that still holds the earlier call's partials; the last has one query per head and
+takes the one-query partial kernel.
 """
 
 import ctypes
@@ -39,7 +40,8 @@ def _noalloc_raw(q, k, v, scale, causal, n_splits):
 @pytest.mark.parametrize("causal", [True, False])
 def test_noalloc_matches_workspace_entry(causal):
     dev = need_gpu()
-    cases = [(2, 8, 16, 4096, 128, 24), (1, 3, 5, 1000, 64, 7)]  # second call: smaller input
+    # each call smaller than the one before; the last takes the one-query kernel
+    cases = [(2, 8, 16, 4096, 128, 24), (1, 3, 5, 1000, 64, 7), (1, 2, 1, 900, 128, 3)]
     for i, (B, H, Nq, Nk, d, n) in enumerate(cases):
         say(f"case noalloc call {i} causal={causal} B={B} H={H} Nq={Nq} Nk={Nk} d={d} n_splits={n}")
         q, k, v = workloads.decode_inputs(B, H, Nq, Nk, d, seed=workloads.SEED_BASE + 8700 + i)
