@@ -675,14 +675,15 @@ hipError_t launch(Params p, hipStream_t st) {
 // causal diagonal run beside the other block's steady state; the ping-pong is faster
 // per key tile once blocks are long.  At d = 128 (with the causal head pairs of the
 // kernel's dispatch) the two met near causal N = 10240 (N / 128 key tiles per 256-row
-// block on average) and non-causal N = 4096, and the ping-pong led by 0.5-1.2% above;
-// at d = 64 the 4-wavefront form was faster at every length timed (2048 to 32768).
+// block on average; the ping-pong led by 0.5% at 12288 and 1.7% at 16384) and, for the
+// non-causal builds without key masks, at N = 2048 (ping-pong +2.5% at 4096, +3.7% at
+// 8192); at d = 64 the 4-wavefront form was faster at every length timed (2048 to 32768).
 template <int D, bool CAUSAL, typename E, bool TAIL>
 hipError_t launch_form(const Params& p, hipStream_t st) {
     if constexpr (D == 64) {
         return launch<D, CAUSAL, E, false, TAIL>(p, st);
     } else {
-        const bool pp = CAUSAL ? p.N > 10240 : p.N > 4096;
+        const bool pp = CAUSAL ? p.N > 10240 : p.N > 2048;
         return pp ? launch<D, CAUSAL, E, true, TAIL>(p, st) : launch<D, CAUSAL, E, false, TAIL>(p, st);
     }
 }

@@ -296,12 +296,12 @@ def test_score_jumps(d, causal, f, fn, dtype, tol_o, tol_l):
 
 @pytest.mark.parametrize("fn,dtype,tol_o,tol_l", [("fa_fwd", "bf16", TOL_BF16_O, TOL_BF16_LSE),
                                                    ("fa_fwd_f16", "f16", 5e-3, 1e-3)])
-@pytest.mark.parametrize("N,causal", [(4096, False), (4097, False), (10240, True), (10241, True)])
+@pytest.mark.parametrize("N,causal", [(2048, False), (2049, False), (4096, False), (10240, True), (10241, True)])
 def test_both_block_forms(N, causal, fn, dtype, tol_o, tol_l):
     """The host runs d = 128 with 4-wavefront blocks (two per CU) up to causal N = 10240
-    and non-causal N = 4096, and with the 8-wavefront ping-pong above; these lengths sit
-    on both sides of each switch, in both 16-bit formats.  Sampled rows include both ends
-    and tile edges."""
+    and non-causal N = 2048, and with the 8-wavefront ping-pong above; these lengths sit
+    on both sides of each switch (and N = 4096, ping-pong without key masks), in both
+    16-bit formats.  Sampled rows include both ends and tile edges."""
     dev = need_gpu()
     B, H, d = 1, 2, 128
     q, k, v = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 7400 + N, dtype=dtype)
