@@ -596,6 +596,9 @@ def main():
     ap.add_argument("--records", metavar="SUBSTR[,SUBSTR...]", default=None,
                     help="time only the per-workload records whose name contains one of the given "
                          "substrings and print them (for profiler runs; not the bench line)")
+    ap.add_argument("--loop-seconds", type=float, default=0.0,
+                    help="with --only: run that kernel back to back for this many seconds (for power "
+                         "and clock sampling from outside the process), then exit")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
@@ -672,6 +675,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    if args.loop_seconds > 0:
+        if args.only is None:
+            sys.exit("bench.py: --loop-seconds needs --only")
+        t0, n, mark = time.perf_counter(), 0, 0.0
+        while time.perf_counter() - t0 < args.loop_seconds:
+            for _ in range(20):
+                step()
+            torch.cuda.synchronize()
+            n += 20
+            if time.perf_counter() - t0 >= mark:
+                print(f"loop {args.only}: {n} calls in {time.perf_counter() - t0:.1f} s", flush=True)
+                mark += 5.0
+        print(json.dumps({"only": args.only, "loop_calls": n, "loop_s": round(time.perf_counter() - t0, 2)}))
+        return
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
