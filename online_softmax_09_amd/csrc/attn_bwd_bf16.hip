@@ -24,7 +24,8 @@
 //      P and dS, packed to bf16 as they lie, are the B operands of dV^T += dO^T P and
 //      dK^T += Q^T dS, whose A operands are transposing reads of the dO and Q tiles.
 //      One role computes S, P and dV, the other dP, dS and dK, with P passed through
-//      LDS (see the kernel).
+//      LDS.  At d = 128 the roles run a tile apart with one barrier per tile; at
+//      d = 64 they meet twice per tile (see the two kernels).
 // Computing dQ in its own pass (recomputing S and dP there) keeps every gradient
 // element owned by one lane of one block: no atomics, and results are bitwise
 // repeatable.
@@ -370,9 +371,261 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
 }
 
 // ---------------------------------------------------------------------------------
-// 3. dK and dV.  8 wavefronts, 128 keys: key group kg = wave % 4 owns keys
-//    k0 + 32 kg + l32 (one key per lane), in two roles that share a SIMD (waves w and
-//    w + 4).  Per 64-row tile of Q, dO, LSE and D:
+// 3a. dK and dV at d = 128, the two roles pipelined.  8 wavefronts, 128 keys: key
+//    group kg = wave % 4 owns keys k0 + 32 kg + l32 (one key per lane), in two roles
+//    that share a SIMD (waves w and w + 4).  The roles run one query tile apart, with
+//    one barrier per tile.  In step
+//    s (query tile i = i_begin + s):
+//      role A (w < 4):  S = Q_i K^T, P = exp2(c S - LSE) -> P_i to LDS (fp32), then
+//                       P packed to bf16 and dV^T += dO_i^T P
+//      role B (w >= 4): dS = P_{i-1} (dP - D)_{i-1} with P_{i-1} from LDS and
+//                       (dP - D)_{i-1} kept in registers since the previous step,
+//                       dK^T += Q_{i-1}^T dS;  then (dP - D)_i = dO_i V^T - D_i
+//    Both roles issue 32 matrix instructions per step and neither waits for the other
+//    inside it; the barrier at the end of the step makes P_i visible to role B and
+//    frees the buffers that the next step's copies overwrite.  Role B reads Q_{i-1}
+//    while tile i + 1 is being copied, so Q has three LDS buffers (dO, LSE, D and the
+//    P exchange two each).  After the last step role B finishes its tile alone.  Every
+//    sub-block is computed; P is zero wherever a score is hidden (the mask is applied
+//    once, in role A), so dS, dK and dV need no mask.  Role A runs at raised issue
+//    priority so that its products, whose results its exponentials wait for, go first.
+//    Results are bitwise those of the two-phase kernel below, which is faster at
+//    d = 64: there its 66 KiB of LDS let two blocks share a CU, where this kernel's
+//    five tile buffers and two P buffers (105 KiB at d = 64) leave one.
+// ---------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+    using L = BLayout<D>;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    // Buffers as separate objects, selected at compile time (see the dQ kernel).
+    __shared__ __attribute__((aligned(1024))) char q_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char q_lds1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char q_lds2[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char do_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char do_lds1[L::TILE];
+    __shared__ __attribute__((aligned(16))) f32x4 p_xch0[4][2][4][64];  // [kg][sb][g][lane]
+    __shared__ __attribute__((aligned(16))) f32x4 p_xch1[4][2][4][64];
+    __shared__ __attribute__((aligned(16))) float lse_lds0[kT];
+    __shared__ __attribute__((aligned(16))) float lse_lds1[kT];
+    __shared__ __attribute__((aligned(16))) float dl_lds0[kT];
+    __shared__ __attribute__((aligned(16))) float dl_lds1[kT];
+
+    int bh, kt;
+    block_coords(p, CAUSAL, false, bh, kt);
+    const int N = p.N;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3;
+    const bool role_a = wave < 4;
+    const int64_t head = (int64_t)bh * N * D;
+    const int64_t rowbase = (int64_t)bh * N;
+    const int k0 = kt * kBwdRows;
+    const int kw0 = k0 + 32 * kg;
+    const int my_k = kw0 + (lane & 31);
+    const int k_row = min(my_k, N - 1);  // keys past the end compute garbage, never stored
+
+    const int t_row = tid / L::NCH, t_pos = tid % L::NCH;
+    const int src_off = t_row * L::RB + 16 * (t_pos ^ L::swz(t_row));
+    TileReads<D> rd;
+    rd.init(lane);
+
+    // role A: K fragments (B operand of S = Q K^T); role B: V fragments (dP = dO V^T)
+    bf16x8 frag[KS];
+    load_frag<D>(frag, (role_a ? p.k : p.v) + head, k_row, h);
+
+    f32x16 acc[DB];  // role A: dV^T, role B: dK^T (unscaled)
+#pragma unroll
+    for (int b = 0; b < DB; ++b) acc[b] = f32x16{};
+
+    // query tiles: causal blocks start at the tile holding their first key
+    const int i_begin = CAUSAL ? k0 / kT : 0;
+    const int n_q = (N + kT - 1) / kT;
+    const int n_steps = n_q - i_begin;
+
+    // buffers of step s: Q at s mod 3; dO, LSE, D and P at s mod 2
+    auto q_buf = [&](auto b) -> char* {
+        constexpr int B = decltype(b)::value;
+        return B == 0 ? q_lds0 : B == 1 ? q_lds1 : q_lds2;
+    };
+    auto copy_tile = [&](auto s6, int i, bool live) __attribute__((always_inline)) {
+        constexpr int S6 = decltype(s6)::value;
+        tile_to_lds<D, kDkdvThreads>(q_buf(std::integral_constant<int, S6 % 3>{}), p.q + head, i * kT, N, wave,
+                                     src_off, live);
+        tile_to_lds<D, kDkdvThreads>(S6 % 2 ? do_lds1 : do_lds0, p.dout + head, i * kT, N, wave, src_off, live);
+        if (wave == 0) rowvec_to_lds(S6 % 2 ? lse_lds1 : lse_lds0, p.lse2 + rowbase, i * kT, N, lane, live);
+        if (wave == 1) rowvec_to_lds(S6 % 2 ? dl_lds1 : dl_lds0, p.delta + rowbase, i * kT, N, lane, live);
+    };
+    copy_tile(std::integral_constant<int, 0>{}, i_begin, true);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+
+    // End of a step: the next tile has landed (vmcnt(0)), and the barrier publishes P.
+    auto end_step = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+    };
+
+    // Role A, step s (S6 = s mod 6) on query tile i.
+    auto step_a = [&](auto s6, int i) __attribute__((always_inline)) {
+        constexpr int S6 = decltype(s6)::value;
+        copy_tile(std::integral_constant<int, (S6 + 1) % 6>{}, i + 1, i + 1 < n_q);
+        const char* qt = q_buf(std::integral_constant<int, S6 % 3>{});
+        const char* dt = S6 % 2 ? do_lds1 : do_lds0;
+        const float* lse_t = S6 % 2 ? lse_lds1 : lse_lds0;
+        f32x4(*xch)[4][64] = S6 % 2 ? p_xch1[kg] : p_xch0[kg];
+        const int i0 = i * kT;
+        f32x16 x[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) x[sb] = rows_times_frag<D, true>(qt, sb, rd, frag);
+        // P of sub-block sb; the mask is a compile-time choice so that whole sub-blocks
+        // (the common case) run without per-element branches
+        auto probs = [&](auto masked_c, int sb) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            // query qs0 + 8 g + 4 h + u is visible when its offset o = 8 g + u from
+            // qs0 + 4 h satisfies o < n_lim and (causal) o >= k_lim
+            const int qb = i0 + 32 * sb + 4 * h;
+            const int n_lim = N - qb, k_lim = my_k - qb;
+            f32x4 l4[4];  // rows 32 sb + 8 g + 4 h + 0..3 of the tile's LSE vector
+#pragma unroll
+            for (int g = 0; g < 4; ++g) l4[g] = *reinterpret_cast<const f32x4*>(&lse_t[32 * sb + 8 * g + 4 * h]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 pv;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int r = 4 * g + u;
+                    float pr = fast_exp2(fmaf(x[sb][r], p.c, -l4[g][u]));
+                    if (MASKED) {
+                        const int o = 8 * g + u;
+                        pr = (o < n_lim && (!CAUSAL || o >= k_lim)) ? pr : 0.0f;
+                    }
+                    x[sb][r] = pr;
+                    pv[u] = pr;
+                }
+                xch[sb][g][lane] = pv;
+            }
+        };
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int qs0 = i0 + 32 * sb;
+            if ((CAUSAL && qs0 < kw0 + 31) || qs0 + 32 > N) probs(std::true_type{}, sb);
+            else probs(std::false_type{}, sb);
+        }
+        // dV^T += dO^T P
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            trans_times_packed<D, true>(acc, dt, 2 * sb + 0, rd, pack8(x[sb], 0));
+            trans_times_packed<D, true>(acc, dt, 2 * sb + 1, rd, pack8(x[sb], 1));
+        }
+        end_step();
+    };
+
+    // Role B: (dP - D) of the previous tile, carried across the barrier.
+    f32x16 xb[2];
+    // dS = P (dP - D) and dK^T += Q^T dS for the tile of step s - 1 (S6 = s mod 6).
+    auto finish_b = [&](auto s6) __attribute__((always_inline)) {
+        constexpr int S6 = decltype(s6)::value;
+        const char* qp = q_buf(std::integral_constant<int, (S6 + 2) % 3>{});
+        f32x4(*xch)[4][64] = (S6 + 1) % 2 ? p_xch1[kg] : p_xch0[kg];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            f32x4 pv[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) pv[g] = xch[sb][g][lane];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xb[sb][4 * g + u] *= pv[g][u];
+            trans_times_packed<D, true>(acc, qp, 2 * sb + 0, rd, pack8(xb[sb], 0));
+            trans_times_packed<D, true>(acc, qp, 2 * sb + 1, rd, pack8(xb[sb], 1));
+        }
+    };
+    auto step_b = [&](auto s6, auto prev, int i) __attribute__((always_inline)) {
+        constexpr int S6 = decltype(s6)::value;
+        copy_tile(std::integral_constant<int, (S6 + 1) % 6>{}, i + 1, i + 1 < n_q);
+        if constexpr (decltype(prev)::value) finish_b(s6);
+        __builtin_amdgcn_sched_barrier(0);
+        const char* dt = S6 % 2 ? do_lds1 : do_lds0;
+        const float* dl_t = S6 % 2 ? dl_lds1 : dl_lds0;
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            xb[sb] = rows_times_frag<D, true>(dt, sb, rd, frag);
+            f32x4 d4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) d4[g] = *reinterpret_cast<const f32x4*>(&dl_t[32 * sb + 8 * g + 4 * h]);
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) xb[sb][4 * g + u] -= d4[g][u];
+        }
+        end_step();
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    // Steps 1 .. n_steps - 1 in groups of six, so that every buffer index is a
+    // compile-time constant, then the remaining zero to five steps.
+    const int n6 = (n_steps - 1) / 6;
+    const int r6 = (n_steps - 1) % 6;
+    if (role_a) {
+        __builtin_amdgcn_s_setprio(1);
+        step_a(I0{}, i_begin);
+        int i = i_begin + 1;
+        for (int g = 0; g < n6; ++g, i += 6) {
+            step_a(I1{}, i);
+            step_a(I2{}, i + 1);
+            step_a(I3{}, i + 2);
+            step_a(I4{}, i + 3);
+            step_a(I5{}, i + 4);
+            step_a(I0{}, i + 5);
+        }
+        if (r6 > 0) step_a(I1{}, i);
+        if (r6 > 1) step_a(I2{}, i + 1);
+        if (r6 > 2) step_a(I3{}, i + 2);
+        if (r6 > 3) step_a(I4{}, i + 3);
+        if (r6 > 4) step_a(I5{}, i + 4);
+        __builtin_amdgcn_s_setprio(0);
+    } else {
+        step_b(I0{}, std::false_type{}, i_begin);
+        int i = i_begin + 1;
+        for (int g = 0; g < n6; ++g, i += 6) {
+            step_b(I1{}, std::true_type{}, i);
+            step_b(I2{}, std::true_type{}, i + 1);
+            step_b(I3{}, std::true_type{}, i + 2);
+            step_b(I4{}, std::true_type{}, i + 3);
+            step_b(I5{}, std::true_type{}, i + 4);
+            step_b(I0{}, std::true_type{}, i + 5);
+        }
+        if (r6 > 0) step_b(I1{}, std::true_type{}, i);
+        if (r6 > 1) step_b(I2{}, std::true_type{}, i + 1);
+        if (r6 > 2) step_b(I3{}, std::true_type{}, i + 2);
+        if (r6 > 3) step_b(I4{}, std::true_type{}, i + 3);
+        if (r6 > 4) step_b(I5{}, std::true_type{}, i + 4);
+        // the last tile (step n_steps - 1), as if in step n_steps
+        switch (n_steps % 6) {
+            case 0: finish_b(I0{}); break;
+            case 1: finish_b(I1{}); break;
+            case 2: finish_b(I2{}); break;
+            case 3: finish_b(I3{}); break;
+            case 4: finish_b(I4{}); break;
+            default: finish_b(I5{}); break;
+        }
+    }
+    if (my_k < N) {
+        if (role_a) store_rows<D>(p.dv + head, my_k, h, acc, 1.0f);
+        else store_rows<D>(p.dk + head, my_k, h, acc, p.scale);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// 3b. dK and dV at d = 64, two phases per tile.  8 wavefronts, 128 keys: key group
+//    kg = wave % 4 owns keys k0 + 32 kg + l32 (one key per lane), in two roles that
+//    share a SIMD (waves w and w + 4).  Per 64-row tile of Q, dO, LSE and D:
 //      phase 1  role A (w < 4):  S = Q K^T, P = exp2(c S - LSE)  -> P to LDS (fp32)
 //               role B (w >= 4): dP = dO V^T, then dP - D
 //      phase 2  role A:  P packed to bf16, dV^T += dO^T P
@@ -384,7 +637,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
 //    that its products, whose results the phase's vector work waits for, go first.
 // ---------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_phased_kernel(BwdParams p) {
     using L = BLayout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
@@ -576,7 +829,11 @@ hipError_t launch_main(BwdParams p, hipStream_t st) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kBwdThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kDkdvThreads), 0, st, p);
+    if constexpr (D == 128)
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kDkdvThreads), 0, st, p);
+    else
+        hipLaunchKernelGGL((attn_bwd_dkdv_phased_kernel<D, CAUSAL>), dim3((unsigned)p.n_blocks), dim3(kDkdvThreads), 0,
+                           st, p);
     return hipGetLastError();
 }
 

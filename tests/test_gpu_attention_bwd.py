@@ -62,7 +62,12 @@ def _compare(tag, got, ref):
 @pytest.mark.parametrize("B,H,N,d,causal", [
     (1, 1, 1, 64, True), (1, 1, 7, 64, False), (1, 2, 64, 64, True), (2, 1, 127, 128, True),
     (1, 2, 128, 128, False), (1, 1, 129, 64, True), (1, 1, 200, 128, True), (2, 2, 383, 64, False),
-    (1, 2, 1000, 128, True), (1, 1, 1000, 64, True), (1, 1, 513, 128, False)])
+    (1, 2, 1000, 128, True), (1, 1, 1000, 64, True), (1, 1, 513, 128, False),
+    # d = 128 runs its query tiles in groups of six steps plus a remainder: blocks of one
+    # step (N = 33; the last key block at N = 129 and 700), every remainder 0..5 (700
+    # causal: 11, 9, 7, 5, 3, 1 steps; 1000 causal: 16, 14, ..., 2), a whole group and
+    # nothing more (448: 7 steps)
+    (1, 1, 33, 128, True), (1, 1, 129, 128, True), (1, 1, 700, 128, True), (1, 1, 448, 128, False)])
 def test_bwd_small_shapes(B, H, N, d, causal):
     dev = need_gpu()
     say(f"case bwd B={B} H={H} N={N} d={d} causal={causal}")
