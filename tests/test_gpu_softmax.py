@@ -60,8 +60,8 @@ def test_one_column_rows_are_exactly_one():
 
 # Every kernel variant: short rows (lane groups), one wavefront per row, four
 # wavefronts per row (LDS merge), streaming; 16-byte and 4-byte paths.
-COLS = [1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 1000, 1023, 1024, 1025,
-        2048, 4095, 4096, 4097, 8192, 12000, 16383, 16384, 16385, 40000, 65536]
+COLS = [1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 1000, 1020, 1023, 1024, 1025,
+        1028, 2048, 4095, 4096, 4097, 8192, 12000, 16383, 16384, 16385, 40000, 65536]
 
 
 @pytest.mark.parametrize("cols", COLS)
