@@ -15,6 +15,7 @@ struct SoftmaxPlan {
     int waves;  // kReg: wavefronts per row (1 or 4)
     int nv;     // kReg: units per lane
     bool vec4;  // 16-byte units (cols % 4 == 0 and both pointers 16-byte aligned)
+    bool head;  // kReg: 16-byte units from each row's first 16-byte boundary, the rest one by one
 };
 
 SoftmaxPlan softmax_plan(const float* x, const float* y, int64_t cols);

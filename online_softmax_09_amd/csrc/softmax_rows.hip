@@ -81,18 +81,38 @@ __global__ __launch_bounds__(256) void softmax_rows_small(const float* x, float*
 // Register-resident rows: WAVES wavefronts per row, NV units (float4 or float) per
 // lane.  Unit u of the row lives in lane (u mod 64*WAVES) of the row's threads.
 // ---------------------------------------------------------------------------
-template <int WAVES, int NV, bool VEC4>
+// HEAD (16-byte units only): rows need not start on a 16-byte boundary.  A row's first
+// boundary lies `head` = 0..3 elements in; the elements before it and the 0..3 after its
+// last whole unit are loaded one each by threads 0 .. head + tail - 1 and go through the
+// same arithmetic as the units.  x and y share their 16-byte phase (the host checks), so
+// the units of y are aligned too.
+template <int WAVES, int NV, bool VEC4, bool HEAD>
 __global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y, int64_t rows,
                                                         int64_t cols) {
+    static_assert(VEC4 || !HEAD, "the head form reads the body in 16-byte units");
     using U = typename Unit<VEC4>::T;
     constexpr int T = 64 * WAVES;        // threads per row
     constexpr int ROWS_PER_BLOCK = 256 / T;
     const int t = threadIdx.x % T;
     const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / T;
     if (row >= rows) return;  // uniform over the row's wavefronts (and the block if WAVES == 4)
-    const int64_t units = VEC4 ? cols / 4 : cols;
-    const U* xr = reinterpret_cast<const U*>(x + row * cols);
-    U* yr = reinterpret_cast<U*>(y + row * cols);
+    const float* xrow = x + row * cols;
+    float* yrow = y + row * cols;
+    int head = 0;
+    int64_t units = VEC4 ? cols / 4 : cols;
+    int64_t e_idx = -1;     // this thread's single element outside the units, if any
+    float ev = kNegInf;
+    if constexpr (HEAD) {
+        head = (int)((0u - (uint32_t)((uintptr_t)xrow >> 2)) & 3u);
+        units = (cols - head) >> 2;
+        const int n_extra = head + (int)((cols - head) & 3);
+        if (t < n_extra) {
+            e_idx = t < head ? t : head + 4 * units + (t - head);
+            ev = __builtin_nontemporal_load(xrow + e_idx);
+        }
+    }
+    const U* xr = reinterpret_cast<const U*>(xrow + head);
+    U* yr = reinterpret_cast<U*>(yrow + head);
 
     U v[NV];
 #pragma unroll
@@ -106,11 +126,12 @@ __global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y
 
     // Lane state over the lane's own elements: m first (all values are in
     // registers), then l = sum exp(x - m); x is replaced by exp(x - m).
-    float m_lane = kNegInf;
+    float m_lane = ev;  // -inf unless the thread holds an element outside the units
 #pragma unroll
     for (int i = 0; i < NV; ++i) m_lane = fmaxf(m_lane, umax(v[i]));
     const float base = safe_base(m_lane);
     float l_lane = 0.0f;
+    if constexpr (HEAD) l_lane = unit_exp_sum(ev, base);
 #pragma unroll
     for (int i = 0; i < NV; ++i) l_lane += unit_exp_sum(v[i], base);
 
@@ -131,6 +152,9 @@ __global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y
     for (int i = 0; i < NV; ++i) {
         const int64_t u = (int64_t)i * T + t;
         if (u < units) __builtin_nontemporal_store(scale_unit(v[i], c), yr + u);
+    }
+    if constexpr (HEAD) {
+        if (e_idx >= 0) __builtin_nontemporal_store(ev * c, yrow + e_idx);
     }
 }
 
@@ -196,7 +220,7 @@ __global__ __launch_bounds__(256) void softmax_rows_stream(const float* x, float
     }
 }
 
-template <int WAVES, bool VEC4>
+template <int WAVES, bool VEC4, bool HEAD>
 hipError_t launch_reg(int nv, const float* x, float* y, int64_t rows, int64_t cols, hipStream_t st) {
     constexpr int rows_per_block = 4 / WAVES;
     const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
@@ -204,8 +228,8 @@ hipError_t launch_reg(int nv, const float* x, float* y, int64_t rows, int64_t co
     const dim3 grid((unsigned)blocks), block(256);
 #define MI355_REG_CASE(NVV)                                                                   \
     case NVV:                                                                                 \
-        hipLaunchKernelGGL((softmax_rows_reg<WAVES, NVV, VEC4>), grid, block, 0, st, x, y, rows, \
-                           cols);                                                             \
+        hipLaunchKernelGGL((softmax_rows_reg<WAVES, NVV, VEC4, HEAD>), grid, block, 0, st, x, y,   \
+                           rows, cols);                                                       \
         break;
     switch (nv) {
         MI355_REG_CASE(1)
@@ -233,8 +257,9 @@ int next_pow2(int64_t n) {
 // Picks the variant for a shape.  Rows of 16-byte units go to four wavefronts beyond 256
 // units (1024 columns): at 1536 to 4096 columns that moved 1.4-6% more bytes per second than
 // one wavefront holding 8 to 16 units per lane, and was even at 8192.  Rows of 4-byte units
-// keep one wavefront up to 1024 units: for short unaligned rows (4096 x 777) four wavefronts
-// of 4 units per lane ran at two thirds of the speed.
+// keep one wavefront up to 1024 units.  Rows off the 16-byte grid take the head form when
+// x and y share a phase: +2.5% to +128% over 4-byte units across the shapes timed (4095
+// columns +5-6%), except 4097 columns (-3%).
 SoftmaxPlan softmax_plan(const float* x, const float* y, int64_t cols) {
     SoftmaxPlan p{};
     if (cols <= 32) {
@@ -242,10 +267,16 @@ SoftmaxPlan softmax_plan(const float* x, const float* y, int64_t cols) {
         p.group = next_pow2(cols);
         return p;
     }
-    p.vec4 = (cols % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
-    const int64_t units = p.vec4 ? cols / 4 : cols;
-    const int nv_max = p.vec4 ? 16 : 64;  // 64 registers of row data per lane
-    const int one_wave_max = p.vec4 ? 4 : 16;  // units per lane on the one-wavefront form
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+    p.vec4 = (cols % 4 == 0) && xa % 16 == 0 && ya % 16 == 0;
+    // Other rows are read in 16-byte units from their first 16-byte boundary on, with up
+    // to three elements on either side taken one by one, when x and y are 4-byte aligned
+    // at the same 16-byte phase (so that the boundaries of x and y rows coincide).
+    p.head = !p.vec4 && xa % 4 == 0 && ya % 4 == 0 && xa % 16 == ya % 16;
+    const bool wide = p.vec4 || p.head;
+    const int64_t units = wide ? cols / 4 : cols;
+    const int nv_max = wide ? 16 : 64;  // 64 registers of row data per lane
+    const int one_wave_max = wide ? 4 : 16;  // units per lane on the one-wavefront form
     if (units <= 64 * one_wave_max) {
         p.kind = SoftmaxPlan::kReg;
         p.waves = 1;
@@ -255,7 +286,8 @@ SoftmaxPlan softmax_plan(const float* x, const float* y, int64_t cols) {
         p.waves = 4;
         p.nv = next_pow2((units + 255) / 256);
     } else {
-        p.kind = SoftmaxPlan::kStream;
+        p.kind = SoftmaxPlan::kStream;  // reads rows that are not whole units in 4-byte units
+        p.head = false;
     }
     return p;
 }
@@ -280,10 +312,12 @@ hipError_t launch_softmax_rows(const float* x, float* y, int64_t rows, int64_t c
         }
         case SoftmaxPlan::kReg:
             if (p.waves == 1)
-                return p.vec4 ? launch_reg<1, true>(p.nv, x, y, rows, cols, st)
-                              : launch_reg<1, false>(p.nv, x, y, rows, cols, st);
-            return p.vec4 ? launch_reg<4, true>(p.nv, x, y, rows, cols, st)
-                          : launch_reg<4, false>(p.nv, x, y, rows, cols, st);
+                return p.head   ? launch_reg<1, true, true>(p.nv, x, y, rows, cols, st)
+                       : p.vec4 ? launch_reg<1, true, false>(p.nv, x, y, rows, cols, st)
+                                : launch_reg<1, false, false>(p.nv, x, y, rows, cols, st);
+            return p.head   ? launch_reg<4, true, true>(p.nv, x, y, rows, cols, st)
+                   : p.vec4 ? launch_reg<4, true, false>(p.nv, x, y, rows, cols, st)
+                            : launch_reg<4, false, false>(p.nv, x, y, rows, cols, st);
         case SoftmaxPlan::kStream: {
             if (rows > 0x7fffffff) return hipErrorInvalidValue;
             const dim3 grid((unsigned)rows), block(256);

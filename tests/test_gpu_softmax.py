@@ -98,21 +98,41 @@ def test_in_place():
     assert ea <= TOL_F32
 
 
-@pytest.mark.parametrize("cols", [4096, 1000, 7])
-def test_unaligned_rows(cols):
-    # Base pointer offset by one float: the 16-byte path must not be taken.
+# Rows off the 16-byte grid.  x and y at the same 16-byte phase (equal offsets) take the
+# head form (16-byte units from each row's first boundary, up to three elements on either
+# side one by one); different phases take 4-byte units; rows past the register forms
+# stream in 4-byte units.
+@pytest.mark.parametrize("cols,x_off,y_off", [
+    (4096, 1, 1), (1000, 1, 1), (7, 1, 1), (33, 2, 2), (35, 2, 2), (1023, 3, 3), (4095, 0, 0),
+    (4095, 1, 1), (4097, 2, 2), (4095, 1, 2), (1000, 0, 3), (40001, 1, 1), (40000, 1, 3)])
+def test_unaligned_rows(cols, x_off, y_off):
     dev = need_gpu()
     rows = 64
     x, _ = workloads.softmax_inputs(rows, cols, seed=workloads.SEED_BASE + 4300 + cols)
-    say(f"case unaligned rows={rows} cols={cols}")
-    buf = torch.empty(rows * cols + 1, dtype=torch.float32, device=dev)
-    xd = buf[1:].view(rows, cols)
+    say(f"case unaligned rows={rows} cols={cols} x_off={x_off} y_off={y_off}")
+    buf = torch.empty(rows * cols + x_off, dtype=torch.float32, device=dev)
+    xd = buf[x_off:].view(rows, cols)
     xd.copy_(x.to(dev))
-    obuf = torch.empty(rows * cols + 1, dtype=torch.float32, device=dev)
-    yd = obuf[1:].view(rows, cols)
+    obuf = torch.empty(rows * cols + y_off, dtype=torch.float32, device=dev)
+    yd = obuf[y_off:].view(rows, cols)
     osm.online_softmax_rows(xd, out=yd)
     torch.cuda.synchronize()
     ea, _ = _oracle_err(x, yd.cpu())
+    assert ea <= TOL_F32
+
+
+def test_in_place_unaligned():
+    dev = need_gpu()
+    rows, cols = 300, 4095
+    x, _ = workloads.softmax_inputs(rows, cols, seed=workloads.SEED_BASE + 4250)
+    say("case in place, unaligned 300 x 4095 at offset 1")
+    buf = torch.empty(rows * cols + 1, dtype=torch.float32, device=dev)
+    xd = buf[1:].view(rows, cols)
+    xd.copy_(x.to(dev))
+    out = osm.online_softmax_rows(xd, out=xd)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == xd.data_ptr()
+    ea, _ = _oracle_err(x, xd.cpu())
     assert ea <= TOL_F32
 
 
