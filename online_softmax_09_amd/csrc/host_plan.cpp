@@ -21,7 +21,8 @@ bool norm_vec_path(bool layer, const void* x, const void* res, const void* gamma
            (!res_out || aligned16(res_out)) && (!layer || aligned16(beta));
 }
 
-// A block keeps at most 16 units per thread of a row in registers.
+// Rows of up to 16 x 256 units are accepted; the kernel holds them in registers (at most
+// 8 units per thread with 512 threads per row, 16 with 256 on the 2-byte path).
 int64_t norm_rows_max_cols(bool layer, const void* x, const void* res, const void* gamma, const void* beta,
                            const void* y, const void* res_out, int64_t cols) {
     return norm_vec_path(layer, x, res, gamma, beta, y, res_out, cols) ? 16 * kNormRowThreads * 8

@@ -9,10 +9,12 @@
 // through HBM.  Here h = x + residual is formed in float32, written back as the updated
 // residual stream (bf16), and normalised from the float32 values.
 //
-// gfx950 mapping: one block of 256 threads (4 wavefronts) per row.  Each thread loads
-// NV units of 8 bf16 (16 bytes) spaced 256 units apart, so every load instruction of the
-// block covers 4 KiB of the row contiguously, and keeps h in registers: the row is read
-// once and written once.  LayerNorm statistics are exact two-pass values per thread (the
+// gfx950 mapping: one block per row, of 128 threads for rows of up to 256 units and 512
+// above (256 on the 2-byte path).  Each thread loads NV units of 8 bf16 (16 bytes) spaced
+// one block-width apart, so every load instruction of the block covers a contiguous
+// stretch of the row (2 KiB or 8 KiB), and keeps h in registers: the row is read once and
+// written once.
+// LayerNorm statistics are exact two-pass values per thread (the
 // thread's own mean, then the sum of squared deviations from it, both from registers),
 // merged across threads with Chan's pairwise rule
 //     n = n_a + n_b,  mu = mu_a + (mu_b - mu_a) n_b / n,
@@ -29,7 +31,6 @@
 namespace mi355 {
 namespace {
 
-constexpr int kNormThreads = kNormRowThreads;
 
 struct NormParams {
     const uint16_t* x;
@@ -57,10 +58,11 @@ __device__ __forceinline__ Welford chan_merge(Welford a, Welford b) {
     return Welford{n, fmaf(d, fb, a.mean), a.m2 + b.m2 + d * d * a.n * fb};
 }
 
-// U = elements per unit (8: 16-byte vectors, 1: scalars); NV = units per thread.
-template <bool LAYER, int U, int NV>
-__global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
-    __shared__ float sh[3][kNormThreads / 64];
+// U = elements per unit (8: 16-byte vectors, 1: scalars); NV = units per thread;
+// THREADS = threads per row (one block).
+template <bool LAYER, int U, int NV, int THREADS>
+__global__ __launch_bounds__(THREADS) void norm_rows_kernel(NormParams p) {
+    __shared__ float sh[3][THREADS / 64];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t cols = p.cols;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
     int nvalid = 0;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t u = tid + (int64_t)kNormThreads * i;
+        const int64_t u = tid + (int64_t)THREADS * i;
         if (u < units) {
             ++nvalid;
             if constexpr (U == 8) {
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
         __syncthreads();
         Welford t{sh[0][0], sh[1][0], sh[2][0]};
 #pragma unroll
-        for (int k = 1; k < kNormThreads / 64; ++k) t = chan_merge(t, Welford{sh[0][k], sh[1][k], sh[2][k]});
+        for (int k = 1; k < THREADS / 64; ++k) t = chan_merge(t, Welford{sh[0][k], sh[1][k], sh[2][k]});
         mean = t.mean;
         rstd = rsqrtf(t.m2 / (float)cols + p.eps);
     } else {
@@ -149,14 +151,14 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
         __syncthreads();
         float tot = 0.0f;
 #pragma unroll
-        for (int k = 0; k < kNormThreads / 64; ++k) tot += sh[0][k];
+        for (int k = 0; k < THREADS / 64; ++k) tot += sh[0][k];
         rstd = rsqrtf(tot / (float)cols + p.eps);
     }
 
     // ---- normalise and store
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t u = tid + (int64_t)kNormThreads * i;
+        const int64_t u = tid + (int64_t)THREADS * i;
         if (u >= units) continue;
         if constexpr (U == 8) {
             const u32x4 gv = *reinterpret_cast<const u32x4*>(p.gamma + 8 * u);
@@ -178,18 +180,35 @@ __global__ __launch_bounds__(kNormThreads) void norm_rows_kernel(NormParams p) {
     }
 }
 
-template <bool LAYER, int U>
+template <bool LAYER, int U, int THREADS>
 hipError_t launch_u(const NormParams& p, int64_t rows, int nv, hipStream_t st) {
-    const dim3 grid((unsigned)rows), block(kNormThreads);
+    const dim3 grid((unsigned)rows), block(THREADS);
     switch (nv) {
-        case 1: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 1>), grid, block, 0, st, p); break;
-        case 2: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 2>), grid, block, 0, st, p); break;
-        case 4: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 4>), grid, block, 0, st, p); break;
-        case 8: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 8>), grid, block, 0, st, p); break;
-        case 16: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 16>), grid, block, 0, st, p); break;
+        case 1: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 1, THREADS>), grid, block, 0, st, p); break;
+        case 2: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 2, THREADS>), grid, block, 0, st, p); break;
+        case 4: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 4, THREADS>), grid, block, 0, st, p); break;
+        case 8: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 8, THREADS>), grid, block, 0, st, p); break;
+        case 16: hipLaunchKernelGGL((norm_rows_kernel<LAYER, U, 16, THREADS>), grid, block, 0, st, p); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <bool LAYER, int U>
+hipError_t launch_threads(const NormParams& p, int64_t rows, int64_t units, hipStream_t st) {
+    // Threads per row from interleaved timings (GB/s, RMSNorm / LayerNorm, two boxes),
+    // 16-byte units: 128 threads for rows of at most 256 units, 512 above.  Against 256
+    // threads for every row: 8192 columns 6188 / 6038 against 5906 / 5734; 4096 +2-3%;
+    // 16384 +8% / +1.5%; 32768 +7% / +4%; 1024 +2% / +26%; 512 +22% / +61%; 2048 within
+    // 1.3%.  LayerNorm fell to 40-70% with 1024 threads, and with 512 on rows of 256 units.
+    // Rows of 2-byte units keep 256 threads (4095 columns: 5-10% slower with 512).
+    const int threads = U == 1 ? 256 : units <= 256 ? 128 : 512;
+    const int64_t per = (units + threads - 1) / threads;
+    int nv = 1;
+    while (nv < per) nv *= 2;
+    if (nv > 16) return hipErrorInvalidValue;
+    if constexpr (U == 1) return launch_u<LAYER, U, 256>(p, rows, nv, st);
+    return threads == 128 ? launch_u<LAYER, U, 128>(p, rows, nv, st) : launch_u<LAYER, U, 512>(p, rows, nv, st);
 }
 
 }  // namespace
@@ -207,12 +226,8 @@ hipError_t launch_norm_rows(bool layer, const void* x, const void* res, const vo
     p.eps = eps;
     const bool vec = norm_vec_path(layer, x, res, gamma, beta, y, res_out, cols);
     const int64_t units = vec ? cols / 8 : cols;
-    const int64_t per = (units + kNormThreads - 1) / kNormThreads;
-    int nv = 1;
-    while (nv < per) nv *= 2;
-    if (nv > 16) return hipErrorInvalidValue;
-    if (layer) return vec ? launch_u<true, 8>(p, rows, nv, st) : launch_u<true, 1>(p, rows, nv, st);
-    return vec ? launch_u<false, 8>(p, rows, nv, st) : launch_u<false, 1>(p, rows, nv, st);
+    if (layer) return vec ? launch_threads<true, 8>(p, rows, units, st) : launch_threads<true, 1>(p, rows, units, st);
+    return vec ? launch_threads<false, 8>(p, rows, units, st) : launch_threads<false, 1>(p, rows, units, st);
 }
 
 }  // namespace mi355
