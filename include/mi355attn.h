@@ -179,7 +179,7 @@ int64_t fa_bwd_workspace_bytes(int B, int H, int N);
  *              trailing parts may be empty.  The call runs B*H*n_splits blocks of four
  *              wavefronts when Nq = 1, else B*H*ceil(Nq/32)*n_splits one-wavefront blocks (up
  *              to five per CU); counts that give every CU an equal share in one round stream
- *              fastest (one block per CU at Nq = 1, three per CU at Nq = 16 on 256 CUs).
+ *              fastest (one block per CU at Nq = 1, two per CU at Nq = 16 on 256 CUs).
  *   d, scale, stream  as for fa_fwd.
  * o, lse and workspace must not overlap each other or any input.
  * Arithmetic: with Nq > 1 the products run on bf16 matrix cores with float32 accumulation

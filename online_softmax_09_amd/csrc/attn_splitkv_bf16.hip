@@ -15,7 +15,11 @@
 // HBM; each wavefront keeps its own two 32-key K and V sub-tile buffers in LDS (32 KiB at
 // d = 128), fed by buffer_load ... lds copies issued one sub-tile ahead, so a block needs
 // no barrier and five blocks fit a CU, which keeps enough bytes in flight (measured
-// better than deeper rings with fewer blocks).  The products are the
+// better than deeper rings with fewer blocks).  The buffers are separate LDS objects
+// picked at compile time, so that the wait before a sub-tile's reads is the one the
+// kernel states: for grids of under two blocks per CU the next sub-tile's copies stay in
+// flight during the reads; otherwise its K copy is waited for as well (measured faster
+// there, see launch_partial).  The products are the
 // forward's: S^T = K Q^T with the Q fragments in registers (one query per lane column;
 // columns past N_q compute garbage and are not stored) and O^T += V^T P^T with V^T read
 // by the transposing LDS load.  The running maximum follows the pages' rule exactly
@@ -29,7 +33,9 @@
 // the output columns and a lane of the parts.  Each lane loads its parts' LSEs and
 // output chunks in one round of independent loads and keeps a running (m, l, O) state;
 // the lanes' states then merge through LDS with the same rescaling rule.
+#include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "launchers.hpp"
@@ -45,7 +51,6 @@ namespace mi355 {
 namespace {
 
 constexpr int kSK = 32;       // keys per sub-tile (one MFMA row block)
-constexpr int kStages = 2;    // LDS buffers per wavefront
 constexpr int kQT = 32;       // queries per wavefront
 constexpr int kPartTile = 64; // part boundaries are multiples of this many keys
 
@@ -103,13 +108,18 @@ __device__ __forceinline__ void subtile_to_lds(char* lds, const uint16_t* head, 
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DEEP>
 __global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams p) {
     using L = SLayout<D>;
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(1024))) char k_lds[kStages][L::TILE];
-    __shared__ __attribute__((aligned(1024))) char v_lds[kStages][L::TILE];
+    // Two K and two V buffers as separate objects, picked at compile time: with one
+    // [2][TILE] array indexed at run time the compiler cannot tell the buffer being read
+    // from the one the next copy is filling, and waits for that copy before every read.
+    __shared__ __attribute__((aligned(1024))) char k_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[L::TILE];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[L::TILE];
 
     // block -> (head bh, query tile qt, part s); parts of one head are adjacent
     const int64_t bid = blockIdx.x;
@@ -171,22 +181,22 @@ __global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams
         }
         const uint16_t* kh = p.k + khead;
         const uint16_t* vh = p.v + khead;
-#pragma unroll
-        for (int t = 0; t < kStages - 1; ++t) {
-            subtile_to_lds<D, L::K_NP>(k_lds[t], kh, lo + t * kSK, Nk, ck, t < n_t);
-            subtile_to_lds<D, L::V_NP>(v_lds[t], vh, lo + t * kSK, Nk, cv, t < n_t);
-        }
+        subtile_to_lds<D, L::K_NP>(k_lds0, kh, lo, Nk, ck, true);
+        subtile_to_lds<D, L::V_NP>(v_lds0, vh, lo, Nk, cv, true);
 
-        for (int t = 0; t < n_t; ++t) {
+        // sub-tile t in buffer PAR = t % 2 (compile time)
+        auto tile = [&](auto par, int t) __attribute__((always_inline)) {
+            constexpr int PAR = decltype(par)::value;
             {
-                const int tn = t + kStages - 1;  // copy the next sub-tile
-                subtile_to_lds<D, L::K_NP>(k_lds[tn % kStages], kh, lo + tn * kSK, Nk, ck, tn < n_t);
-                subtile_to_lds<D, L::V_NP>(v_lds[tn % kStages], vh, lo + tn * kSK, Nk, cv, tn < n_t);
+                const int tn = t + 1;  // copy the next sub-tile into the other buffer
+                subtile_to_lds<D, L::K_NP>(PAR ? k_lds0 : k_lds1, kh, lo + tn * kSK, Nk, ck, tn < n_t);
+                subtile_to_lds<D, L::V_NP>(PAR ? v_lds0 : v_lds1, vh, lo + tn * kSK, Nk, cv, tn < n_t);
             }
-            // every copy but the newest sub-tile's has landed
-            __builtin_amdgcn_s_waitcnt(vmcnt_enc((kStages - 1) * 2 * L::ROUNDS));
-            const char* kt = k_lds[t % kStages];
-            const char* vt = v_lds[t % kStages];
+            // DEEP: every copy but the next sub-tile's has landed.  Otherwise the next
+            // sub-tile's K copy (issued first) has landed too, and only its V is in flight.
+            __builtin_amdgcn_s_waitcnt(vmcnt_enc((DEEP ? 2 : 1) * L::ROUNDS));
+            const char* kt = PAR ? k_lds1 : k_lds0;
+            const char* vt = PAR ? v_lds1 : v_lds0;
             const int j0 = lo + t * kSK;
             // S^T = K Q^T: lane holds query column l32, keys j0 + 8 (r/4) + 4 h + r%4
             f32x16 st = f32x16{};
@@ -195,35 +205,41 @@ __global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams
                 const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt + k_off[ks]);
                 st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st, 0, 0, 0);
             }
-            const bool masked = j0 + kSK > hi || (CAUSAL && j0 + kSK - 1 > shift + q0);
-            auto visible = [&](int r) {
-                const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
-                return key < hi && key <= key_lim;
+            // the mask is a compile-time choice so that whole sub-tiles (the common case)
+            // run without per-element branches
+            auto softmax = [&](auto masked_c) __attribute__((always_inline)) {
+                constexpr bool MASKED = decltype(masked_c)::value;
+                auto visible = [&](int r) {
+                    const int key = j0 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    return key < hi && key <= key_lim;
+                };
+                float mx = kNegInf;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, (!MASKED || visible(r)) ? st[r] : kNegInf);
+                const HalfPair pm = half_pair(mx);
+                const float mt = fmaxf(pm.lo, pm.hi);
+                const float m_new = mt == kNegInf ? m : fmaxf(m, mt * p.c);
+                const float base = safe_base(m_new);
+                const float alpha = fast_exp2(m - base);  // 0 while m = -inf
+                float sum = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float e = fast_exp2(fmaf(st[r], p.c, -base));
+                    if (MASKED) e = visible(r) ? e : 0.0f;  // hidden keys get exactly 0
+                    st[r] = e;
+                    sum += e;
+                }
+                l = alpha * l + sum;
+                m = m_new;
+                if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+                    for (int b = 0; b < DB; ++b)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+                }
             };
-            float mx = kNegInf;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, (!masked || visible(r)) ? st[r] : kNegInf);
-            const HalfPair pm = half_pair(mx);
-            const float mt = fmaxf(pm.lo, pm.hi);
-            const float m_new = mt == kNegInf ? m : fmaxf(m, mt * p.c);
-            const float base = safe_base(m_new);
-            const float alpha = fast_exp2(m - base);  // 0 while m = -inf
-            float sum = 0.0f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float e = fast_exp2(fmaf(st[r], p.c, -base));
-                if (masked) e = visible(r) ? e : 0.0f;  // hidden keys get exactly 0
-                st[r] = e;
-                sum += e;
-            }
-            l = alpha * l + sum;
-            m = m_new;
-            if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-                for (int b = 0; b < DB; ++b)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
-            }
+            if (j0 + kSK > hi || (CAUSAL && j0 + kSK - 1 > shift + q0)) softmax(std::true_type{});
+            else softmax(std::false_type{});
             // O^T += V^T P^T over the two 16-key groups
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
@@ -238,7 +254,13 @@ __global__ __launch_bounds__(64, 2) void attn_splitkv_partial_kernel(SplitParams
                                                                      acc[b], 0, 0, 0);
                 }
             }
+        };
+        int t = 0;
+        for (; t + 1 < n_t; t += 2) {
+            tile(std::integral_constant<int, 0>{}, t);
+            tile(std::integral_constant<int, 1>{}, t + 1);
         }
+        if (t < n_t) tile(std::integral_constant<int, 0>{}, t);
         __builtin_amdgcn_s_waitcnt(vmcnt_enc(0));  // no copy outlives the block
     }
 
@@ -521,6 +543,39 @@ hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, void*
     return hipErrorInvalidValue;
 }
 
+namespace {
+
+// Compute units of the current device, looked up once per device.
+int cu_count() {
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The partial kernel's copy depth by blocks per CU, from interleaved timings (GB/s,
+// bf16, d = 128): with fewer than two one-wavefront blocks per CU the wavefront keeps
+// its next K and V sub-tiles in flight while it computes (1x32x32x65536 in 8 parts:
+// 5055 against 3379 waiting for the next K; 16 queries x 128 heads x 32768 keys in 3
+// parts: 5782 against 4871); from two per CU on, waiting for the next K as well was as
+// fast or faster (4 parts: 6043 against 5665; 1x32x32x65536 in 16 parts: 5863 against
+// 5715), the other wavefronts covering the wait.
+template <int D, bool CAUSAL>
+hipError_t launch_partial(const SplitParams& p, int64_t blocks, bool deep, hipStream_t st) {
+    if (deep)
+        hipLaunchKernelGGL((attn_splitkv_partial_kernel<D, CAUSAL, true>), dim3((unsigned)blocks), dim3(64), 0, st, p);
+    else
+        hipLaunchKernelGGL((attn_splitkv_partial_kernel<D, CAUSAL, false>), dim3((unsigned)blocks), dim3(64), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                     float* workspace, int B, int H, int Nq, int Nk, int d, float scale, bool causal,
                                     int n_parts, hipStream_t st) {
@@ -547,18 +602,16 @@ hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v,
             hipLaunchKernelGGL((attn_decode_partial_kernel<128>), dim3((unsigned)blocks), dim3(kGvThreads), 0, st, p);
         else
             return hipErrorInvalidValue;
-    } else if (d == 64) {
-        if (causal)
-            hipLaunchKernelGGL((attn_splitkv_partial_kernel<64, true>), dim3((unsigned)blocks), dim3(64), 0, st, p);
-        else
-            hipLaunchKernelGGL((attn_splitkv_partial_kernel<64, false>), dim3((unsigned)blocks), dim3(64), 0, st, p);
-    } else if (d == 128) {
-        if (causal)
-            hipLaunchKernelGGL((attn_splitkv_partial_kernel<128, true>), dim3((unsigned)blocks), dim3(64), 0, st, p);
-        else
-            hipLaunchKernelGGL((attn_splitkv_partial_kernel<128, false>), dim3((unsigned)blocks), dim3(64), 0, st, p);
     } else {
-        return hipErrorInvalidValue;
+        const bool deep = blocks < 2 * (int64_t)cu_count();
+        hipError_t e = hipSuccess;
+        if (d == 64)
+            e = causal ? launch_partial<64, true>(p, blocks, deep, st) : launch_partial<64, false>(p, blocks, deep, st);
+        else if (d == 128)
+            e = causal ? launch_partial<128, true>(p, blocks, deep, st) : launch_partial<128, false>(p, blocks, deep, st);
+        else
+            return hipErrorInvalidValue;
+        if (e != hipSuccess) return e;
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

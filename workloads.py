@@ -56,7 +56,7 @@ CONFIGS = {
                                           d=128, causal=True, n_splits=32, seed=SEED_BASE + 5),
     # A batch of decoding streams with 16 queries each (speculative or chunked decoding).
     "decode_bf16_b4h32q16k32768d128": dict(kind="decode", dtype="bf16", B=4, H=32, Nq=16, Nk=32768,
-                                           d=128, causal=True, n_splits=6, seed=SEED_BASE + 6),
+                                           d=128, causal=True, n_splits=4, seed=SEED_BASE + 6),
     # Residual add + normalisation of 16384 tokens with a hidden size of 8192.
     "norm_bf16_16384x8192": dict(kind="norm", rows=16384, cols=8192, eps=1e-5, seed=SEED_BASE + 7),
 }
