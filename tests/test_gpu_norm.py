@@ -37,8 +37,10 @@ def _check(tag, y, h, y_ref, h_ref):
 
 
 @pytest.mark.parametrize("layer", [False, True])
-@pytest.mark.parametrize("rows,cols", [(1, 8), (3, 64), (7, 1000), (5, 4096), (2, 8192), (3, 32768), (4, 4095),
-                                       (9, 1), (2, 24)])
+# 16-byte rows take 128 threads up to 256 units (2048 columns) and 512 above (2056: 257
+# units, one per thread, the other 255 threads idle); 2-byte rows (1000, 4095, 24, 1) take 256.
+@pytest.mark.parametrize("rows,cols", [(1, 8), (3, 64), (7, 1000), (4, 2048), (4, 2056), (5, 4096), (2, 8192),
+                                       (3, 32768), (4, 4095), (9, 1), (2, 24)])
 def test_norm_shapes(layer, rows, cols):
     dev = need_gpu()
     say(f"case norm layer={layer} rows={rows} cols={cols}")
