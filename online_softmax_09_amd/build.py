@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmi355attn.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["api.cpp", "host_plan.cpp", "softmax_rows.hip", "attn_fwd_f32.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_splitkv_bf16.hip", "norm_rows.hip"]
+SOURCES = ["api.cpp", "host_plan.cpp", "device_info.cpp", "softmax_rows.hip", "attn_fwd_f32.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "attn_splitkv_bf16.hip", "norm_rows.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

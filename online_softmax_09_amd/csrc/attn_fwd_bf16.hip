@@ -56,7 +56,6 @@
 //     stream of a head is then shared through that XCD's L2.  In causal mode an XCD
 //     takes its heads in pairs and runs each pair's query tiles longest first across
 //     the pair (at d = 64 the shortest quarter of every head's tiles comes last).
-#include <atomic>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -624,19 +623,6 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
     }
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static std::atomic<int> cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cus[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // Blocks of equal length (non-causal) run in rounds of `occ` per CU.  With three
 // 4-wavefront blocks per CU a CU does about 5% more work per unit time than with two,
 // and a lone block (one wavefront per SIMD) about 25% less; the last, partial round
@@ -662,7 +648,7 @@ hipError_t launch(Params p, hipStream_t st) {
     // when that finishes sooner.
     unsigned lds_pad = 0;
     if constexpr (D == 64 && !CAUSAL && !TAIL) {
-        const int cus = device_cus();
+        const int cus = device_cu_count();
         if (two_per_cu_faster((blocks + cus - 1) / cus)) lds_pad = 24 << 10;
     }
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, E, PP, TAIL>), dim3((unsigned)p.n_blocks),

@@ -33,7 +33,6 @@
 // the output columns and a lane of the parts.  Each lane loads its parts' LSEs and
 // output chunks in one round of independent loads and keeps a running (m, l, O) state;
 // the lanes' states then merge through LDS with the same rescaling rule.
-#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -545,19 +544,6 @@ hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, void*
 
 namespace {
 
-// Compute units of the current device, looked up once per device.
-int cu_count() {
-    static std::atomic<int> cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cus[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 // The partial kernel's copy depth by blocks per CU, from interleaved timings (GB/s,
 // bf16, d = 128): with fewer than two one-wavefront blocks per CU the wavefront keeps
 // its next K and V sub-tiles in flight while it computes (1x32x32x65536 in 8 parts:
@@ -603,7 +589,7 @@ hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v,
         else
             return hipErrorInvalidValue;
     } else {
-        const bool deep = blocks < 2 * (int64_t)cu_count();
+        const bool deep = blocks < 2 * (int64_t)device_cu_count();
         hipError_t e = hipSuccess;
         if (d == 64)
             e = causal ? launch_partial<64, true>(p, blocks, deep, st) : launch_partial<64, false>(p, blocks, deep, st);

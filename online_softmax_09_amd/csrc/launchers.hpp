@@ -55,6 +55,9 @@ hipError_t launch_attn_merge(const float* o_parts, const float* lse_parts, void*
 // these pointers (rows of a multiple of 8 with 16-byte aligned pointers use 16-byte units).
 // Threads per row block of the norm kernel.  norm_vec_path: whether a call takes the
 // 16-byte path (host logic in host_plan.cpp, shared by the argument checks and the launch).
+// Compute units of the current device (256 if the runtime cannot say), cached per device.
+int device_cu_count();
+
 constexpr int kNormRowThreads = 256;
 bool norm_vec_path(bool layer, const void* x, const void* res, const void* gamma, const void* beta, const void* y,
                    const void* res_out, int64_t cols);
