@@ -31,7 +31,10 @@ def _gpu_splitkv(q, k, v, scale, causal, n_splits, dev):
     (1, 1, 32, 4096, 128, True, 16), (1, 2, 40, 300, 64, False, 3), (1, 1, 1, 1, 64, True, 1),
     (1, 1, 3, 3, 128, True, 2), (1, 1, 1, 64, 128, True, 8), (1, 1, 7, 100, 64, True, 4096),
     (2, 2, 16, 2049, 128, True, 32), (1, 1, 33, 33, 128, True, 3), (1, 2, 70, 50, 128, False, 2),
-    (1, 3, 1, 4999, 64, False, 5), (2, 2, 1, 3000, 128, True, 40), (1, 1, 1, 300, 64, True, 64)])
+    (1, 3, 1, 4999, 64, False, 5), (2, 2, 1, 3000, 128, True, 40), (1, 1, 1, 300, 64, True, 64),
+    # at least two blocks per CU on 256 CUs (512 blocks): the multi-query kernel waits for
+    # the next K copy as well as the current sub-tile's (the cases above keep both in flight)
+    (2, 64, 20, 2000, 64, True, 4), (1, 128, 33, 2049, 128, True, 2), (1, 128, 40, 1500, 64, False, 2)])
 def test_splitkv_shapes(B, H, Nq, Nk, d, causal, n_splits):
     dev = need_gpu()
     say(f"case splitkv B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal} n_splits={n_splits}")
