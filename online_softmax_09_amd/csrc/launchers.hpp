@@ -12,7 +12,7 @@ namespace mi355 {
 struct SoftmaxPlan {
     enum Kind { kSmall, kReg, kStream } kind;
     int group;  // kSmall: lanes per row
-    int waves;  // kReg: wavefronts per row (1 or 4)
+    int waves;  // kReg: wavefronts per row (1, 4 or 8)
     int nv;     // kReg: units per lane
     bool vec4;  // 16-byte units (cols % 4 == 0 and both pointers 16-byte aligned)
     bool head;  // kReg: 16-byte units from each row's first 16-byte boundary, the rest one by one

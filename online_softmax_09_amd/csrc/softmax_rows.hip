@@ -87,12 +87,12 @@ __global__ __launch_bounds__(256) void softmax_rows_small(const float* x, float*
 // same arithmetic as the units.  x and y share their 16-byte phase (the host checks), so
 // the units of y are aligned too.
 template <int WAVES, int NV, bool VEC4, bool HEAD>
-__global__ __launch_bounds__(256) void softmax_rows_reg(const float* x, float* y, int64_t rows,
-                                                        int64_t cols) {
+__global__ __launch_bounds__(WAVES > 4 ? 64 * WAVES : 256) void softmax_rows_reg(const float* x, float* y,
+                                                                                int64_t rows, int64_t cols) {
     static_assert(VEC4 || !HEAD, "the head form reads the body in 16-byte units");
     using U = typename Unit<VEC4>::T;
     constexpr int T = 64 * WAVES;        // threads per row
-    constexpr int ROWS_PER_BLOCK = 256 / T;
+    constexpr int ROWS_PER_BLOCK = (WAVES > 4 ? T : 256) / T;  // a block of 256 threads, or one row
     const int t = threadIdx.x % T;
     const int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / T;
     if (row >= rows) return;  // uniform over the row's wavefronts (and the block if WAVES == 4)
@@ -222,10 +222,10 @@ __global__ __launch_bounds__(256) void softmax_rows_stream(const float* x, float
 
 template <int WAVES, bool VEC4, bool HEAD>
 hipError_t launch_reg(int nv, const float* x, float* y, int64_t rows, int64_t cols, hipStream_t st) {
-    constexpr int rows_per_block = 4 / WAVES;
+    constexpr int rows_per_block = WAVES > 4 ? 1 : 4 / WAVES;
     const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)blocks), block(256);
+    const dim3 grid((unsigned)blocks), block(WAVES > 4 ? 64 * WAVES : 256);
 #define MI355_REG_CASE(NVV)                                                                   \
     case NVV:                                                                                 \
         hipLaunchKernelGGL((softmax_rows_reg<WAVES, NVV, VEC4, HEAD>), grid, block, 0, st, x, y,   \
@@ -256,7 +256,10 @@ int next_pow2(int64_t n) {
 
 // Picks the variant for a shape.  Rows of 16-byte units go to four wavefronts beyond 256
 // units (1024 columns): at 1536 to 4096 columns that moved 1.4-6% more bytes per second than
-// one wavefront holding 8 to 16 units per lane, and was even at 8192.  Rows of 4-byte units
+// one wavefront holding 8 to 16 units per lane, and was even at 8192.  From 769 to 1024
+// units (3076 to 4096 columns) eight wavefronts of 2 units per lane, in a block of its own,
+// were faster again: 3584 +2.5%, 3840 +10%, 4000 +15%, 4096 +3-4%, 4095 +11%; at 768 units
+// and below, and at 1536 and 2048, they were slower (2052 columns -26%, 8192 -5%).  Rows of 4-byte units
 // keep one wavefront up to 1024 units.  Rows off the 16-byte grid take the head form when
 // x and y share a phase: +2.5% to +128% over 4-byte units across the shapes timed (4095
 // columns +5-6%), except 4097 columns (-3%).
@@ -281,6 +284,10 @@ SoftmaxPlan softmax_plan(const float* x, const float* y, int64_t cols) {
         p.kind = SoftmaxPlan::kReg;
         p.waves = 1;
         p.nv = next_pow2((units + 63) / 64);
+    } else if (wide && units > 768 && units <= 1024) {
+        p.kind = SoftmaxPlan::kReg;
+        p.waves = 8;
+        p.nv = 2;
     } else if (units <= 256 * (int64_t)nv_max) {
         p.kind = SoftmaxPlan::kReg;
         p.waves = 4;
@@ -315,6 +322,9 @@ hipError_t launch_softmax_rows(const float* x, float* y, int64_t rows, int64_t c
                 return p.head   ? launch_reg<1, true, true>(p.nv, x, y, rows, cols, st)
                        : p.vec4 ? launch_reg<1, true, false>(p.nv, x, y, rows, cols, st)
                                 : launch_reg<1, false, false>(p.nv, x, y, rows, cols, st);
+            if (p.waves == 8)  // 16-byte units only
+                return p.head ? launch_reg<8, true, true>(p.nv, x, y, rows, cols, st)
+                              : launch_reg<8, true, false>(p.nv, x, y, rows, cols, st);
             return p.head   ? launch_reg<4, true, true>(p.nv, x, y, rows, cols, st)
                    : p.vec4 ? launch_reg<4, true, false>(p.nv, x, y, rows, cols, st)
                             : launch_reg<4, false, false>(p.nv, x, y, rows, cols, st);

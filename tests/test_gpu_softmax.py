@@ -58,10 +58,11 @@ def test_one_column_rows_are_exactly_one():
     assert torch.all(y == 1.0)
 
 
-# Every kernel variant: short rows (lane groups), one wavefront per row, four
-# wavefronts per row (LDS merge), streaming; 16-byte and 4-byte paths.
+# Every kernel variant: short rows (lane groups), one wavefront per row, four and eight
+# wavefronts per row (LDS merge; eight from 769 to 1024 16-byte units, e.g. 3076-4096
+# columns), streaming; 16-byte, head-form and 4-byte paths.
 COLS = [1, 2, 3, 5, 16, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 1000, 1020, 1023, 1024, 1025,
-        1028, 2048, 4095, 4096, 4097, 8192, 12000, 16383, 16384, 16385, 40000, 65536]
+        1028, 2048, 3072, 3073, 3076, 4095, 4096, 4097, 8192, 12000, 16383, 16384, 16385, 40000, 65536]
 
 
 @pytest.mark.parametrize("cols", COLS)
