@@ -592,9 +592,11 @@ hipError_t launch_attn_splitkv_bf16(const void* q, const void* k, const void* v,
         const bool deep = blocks < 2 * (int64_t)device_cu_count();
         hipError_t e = hipSuccess;
         if (d == 64)
-            e = causal ? launch_partial<64, true>(p, blocks, deep, st) : launch_partial<64, false>(p, blocks, deep, st);
+            e = causal ? launch_partial<64, true>(p, blocks, deep, st)
+                       : launch_partial<64, false>(p, blocks, deep, st);
         else if (d == 128)
-            e = causal ? launch_partial<128, true>(p, blocks, deep, st) : launch_partial<128, false>(p, blocks, deep, st);
+            e = causal ? launch_partial<128, true>(p, blocks, deep, st)
+                       : launch_partial<128, false>(p, blocks, deep, st);
         else
             return hipErrorInvalidValue;
         if (e != hipSuccess) return e;

@@ -11,7 +11,7 @@
 //      reduces it to a lane state (m_lane, l_lane) while overwriting x with
 //      e = exp(x - m_lane) in registers;
 //   2. the 64 lane states are merged as a tree across the wavefront (6 levels);
-//   3. for rows spread over 4 wavefronts, the 4 wave states meet in LDS and every
+//   3. for rows spread over 4 or 8 wavefronts, the wave states meet in LDS and every
 //      thread merges them in the same fixed order;
 //   4. y = e * exp(m_lane - m) / l is written from registers.
 //
@@ -255,14 +255,15 @@ int next_pow2(int64_t n) {
 }  // namespace
 
 // Picks the variant for a shape.  Rows of 16-byte units go to four wavefronts beyond 256
-// units (1024 columns): at 1536 to 4096 columns that moved 1.4-6% more bytes per second than
-// one wavefront holding 8 to 16 units per lane, and was even at 8192.  From 769 to 1024
-// units (3076 to 4096 columns) eight wavefronts of 2 units per lane, in a block of its own,
-// were faster again: 3584 +2.5%, 3840 +10%, 4000 +15%, 4096 +3-4%, 4095 +11%; at 768 units
-// and below, and at 1536 and 2048, they were slower (2052 columns -26%, 8192 -5%).  Rows of 4-byte units
-// keep one wavefront up to 1024 units.  Rows off the 16-byte grid take the head form when
-// x and y share a phase: +2.5% to +128% over 4-byte units across the shapes timed (4095
-// columns +5-6%), except 4097 columns (-3%).
+// units (1024 columns): at 1536 to 4096 columns that moved 1.4-6% more bytes per second
+// than one wavefront holding 8 to 16 units per lane, and was even at 8192.  From 769 to
+// 1024 units (3076 to 4096 columns) eight wavefronts of 2 units per lane, in a block of
+// their own, were faster again: 3584 +2.5%, 3840 +10%, 4000 +15%, 4096 +3-4%, 4095 +11%;
+// at 768 units and below, and at 1536 and 2048, they were slower (2052 columns -26%,
+// 8192 -5%).  Rows of 4-byte units keep one wavefront up to 1024 units.  Rows off the
+// 16-byte grid take the head form when x and y share a phase: +2.5% to +128% over 4-byte
+// units across the shapes timed with four wavefronts (4095 columns +5-6%), except 4097
+// columns (-3%).
 SoftmaxPlan softmax_plan(const float* x, const float* y, int64_t cols) {
     SoftmaxPlan p{};
     if (cols <= 32) {
