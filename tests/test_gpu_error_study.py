@@ -10,11 +10,16 @@ to each format (the oracle evaluates the rounded inputs, so only the computation
 is measured):
 
   * max, mean and 99th-percentile absolute error of O, for N = 256 .. 16384 (non-causal,
-    B = 1, H = 2, d = 128; from N = 4096 on, 512 seeded query rows per head);
+    B = 1, H = 2, d = 128; from N = 4096 on, 512 seeded query rows per head), and the
+    root-mean-square error relative to the root-mean-square of O, beside what rounding the
+    exact O once to the output format gives (unit roundoff u = 2^-24, 2^-11, 2^-8 with
+    round-to-nearest: a relative error spread evenly over [-u, u], root mean square u/sqrt 3);
   * bf16 split-KV with 1 .. 256 parts over 16384 keys (256 queries), i.e. 0 .. 255 merges.
 
 It asserts the gates (float32 <= 1e-5, fp16 <= 5e-3, bf16 <= 2e-2), the ordering implied
-by the formats' precisions (float32 < fp16 < bf16 in mean error at every N), and that
+by the formats' precisions (float32 < fp16 < bf16 in mean error at every N), that the fp16
+and bf16 paths add at most a quarter to the error of rounding the exact O once to their
+output format (root-mean-square relative error <= 1.25 u/sqrt 3), and that
 merging partial results in float32 adds no visible error (the largest part count stays
 within 25% + 1e-3 of the single part).  The table is printed for the record.
 """
@@ -31,6 +36,7 @@ from parity import need_gpu, oracle_rows_per_head, say
 pytestmark = pytest.mark.gpu
 
 GATES = {"f32": 1e-5, "f16": 5e-3, "bf16": 2e-2}
+UNIT_ROUNDOFF = {"f32": 2.0**-24, "f16": 2.0**-11, "bf16": 2.0**-8}
 PATH = {"f32": "fa_fwd_f32", "f16": "fa_fwd_f16", "bf16": "fa_fwd"}
 
 
@@ -43,7 +49,7 @@ def test_error_vs_length_and_format():
     dev = need_gpu()
     B, H, d = 1, 2, 128
     scale = workloads.default_scale(d)
-    say("  N      format  max abs    mean abs   p99 abs")
+    say("  N      format  max abs    mean abs   p99 abs    rms rel    output rounding u/sqrt3")
     for N in (256, 1024, 4096, 16384):
         q32, k32, v32 = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 9500 + N, dtype="f32")
         rows = None if N < 4096 else workloads.sampled_query_rows(B, H, N, 510, seed=workloads.SEED_BASE + N)
@@ -61,9 +67,13 @@ def test_error_vs_length_and_format():
                 o_ref, _ = oracle_rows_per_head(q, k, v, scale, False, rows)
                 err = np.take_along_axis(o, rows[..., None], axis=2) - o_ref
             mx, mean, p99 = _stats(err)
+            rms_rel = float(np.sqrt(np.mean(err**2)) / np.sqrt(np.mean(np.asarray(o_ref, dtype=np.float64)**2)))
             means[fmt] = mean
-            say(f"  {N:<6} {fmt:<6}  {mx:.3e}  {mean:.3e}  {p99:.3e}")
+            say(f"  {N:<6} {fmt:<6}  {mx:.3e}  {mean:.3e}  {p99:.3e}  {rms_rel:.3e}  "
+                f"{UNIT_ROUNDOFF[fmt] / np.sqrt(3.0):.3e}")
             assert mx <= GATES[fmt], (N, fmt, mx)
+            if fmt != "f32":
+                assert rms_rel <= 1.25 * UNIT_ROUNDOFF[fmt] / np.sqrt(3.0), (N, fmt, rms_rel)
         assert means["f32"] < means["f16"] < means["bf16"], (N, means)
 
 
