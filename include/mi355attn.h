@@ -36,7 +36,8 @@
  *   Streams    `stream` is a hipStream_t passed as void*; NULL means the default
  *              stream.  Work is enqueued asynchronously on that stream; outputs are
  *              valid once the caller has synchronised with it.  Nothing here
- *              synchronises.
+ *              synchronises, allocates or sets memory, so calls may be captured in a
+ *              HIP graph and replayed.
  *   Errors     Arguments are checked before any HIP call.  A bad argument returns
  *              FA_ERR_INVALID_ARG, an unsupported shape or head dimension
  *              returns FA_ERR_UNSUPPORTED, and a failed launch returns FA_ERR_HIP
