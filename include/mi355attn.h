@@ -124,7 +124,9 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  *   cols  >= 1 and cols <= 1048576 (larger rows return FA_ERR_UNSUPPORTED).
  *
  * Each row is read once from device memory when it fits on chip (cols <= 16384) and twice
- * otherwise; it is written once.  Inputs must be finite.
+ * otherwise; it is written once.  Entries may be -inf (masked: probability exactly 0) as
+ * long as the row holds a finite entry; a row of -inf only has normaliser 0 and gives NaN.
+ * +inf and NaN entries are not supported.
  */
 int online_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream);
 

@@ -153,3 +153,33 @@ def test_repeat_runs_bitwise_identical():
     b = osm.online_softmax_rows(xd)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# Masked entries (-inf) in every kernel variant: lane groups, one, four and eight
+# wavefronts per row, the head form (rows off the 16-byte grid) and the streaming form.
+@pytest.mark.parametrize("cols", [5, 33, 1000, 3072, 4095, 4096, 20000])
+def test_masked_rows(cols):
+    dev = need_gpu()
+    rows = 40
+    x, _ = workloads.softmax_inputs(rows, cols, seed=workloads.SEED_BASE + 4500 + cols, special_frac=0.0)
+    xa = x.numpy().copy()
+    g = np.random.default_rng(workloads.SEED_BASE + 4600 + cols)
+    mask = g.random(size=xa.shape) < 0.5
+    mask[:, g.integers(cols)] = False  # every row keeps a finite entry ...
+    one = int(g.integers(cols))
+    mask[0, :] = True
+    mask[0, one] = False               # ... row 0 exactly one
+    mask[1, : cols // 2] = True        # row 1: the first half masked
+    mask[2, :] = True                  # row 2: nothing finite
+    mask[3, :-1] = True
+    mask[3, -1] = False                # row 3: only the last entry
+    xa[mask] = -np.inf
+    say(f"case masked rows={rows} cols={cols}")
+    y = _run(torch.from_numpy(xa), dev).numpy()
+    assert np.all(np.isnan(y[2])), "a row of -inf only has normaliser 0"
+    live = np.ones(rows, dtype=bool)
+    live[2] = False
+    assert np.all(y[live][mask[live]] == 0.0)
+    assert y[0, one] == 1.0 and y[3, -1] == 1.0
+    ref, _, _ = oracle.softmax_rows(xa[live])
+    assert max_abs(y[live], ref) <= TOL_F32

@@ -328,3 +328,29 @@ def test_pins_catch_softmax_mutants(mutant):
 
 def test_pins_catch_merge_mutant():
     assert not check_merge_order(oracle.online_state, _merge_one_sided)
+
+
+def test_masked_entries():
+    """Entries of -inf (masked) get probability exactly 0, and the others equal the softmax
+    of the finite entries alone (e^-inf = 0 adds nothing to the normaliser); a row with one
+    finite entry is one-hot; a row of -inf only has normaliser 0 and gives NaN."""
+    g = np.random.default_rng(workloads.SEED_BASE + 4700)
+    x = g.normal(0.0, 3.0, size=(6, 50))
+    mask = g.random(size=x.shape) < 0.5
+    mask[:, 7] = False  # every row keeps a finite entry
+    xm = np.where(mask, -np.inf, x)
+    y, m, l = oracle.softmax_rows(xm)
+    assert np.all(y[mask] == 0.0)
+    for r in range(x.shape[0]):
+        keep = ~mask[r]
+        ref, _, _ = oracle.softmax_rows(x[r, keep])
+        np.testing.assert_allclose(y[r, keep], ref, rtol=1e-15, atol=0)
+        ref_t = torch.softmax(torch.from_numpy(xm[r]), dim=0).numpy()
+        np.testing.assert_allclose(y[r], ref_t, rtol=1e-13, atol=1e-300)
+    one = np.full((1, 9), -np.inf)
+    one[0, 4] = 2.5
+    y1, _, _ = oracle.softmax_rows(one)
+    assert y1[0, 4] == 1.0 and np.all(np.delete(y1[0], 4) == 0.0)
+    with np.errstate(invalid="ignore"):
+        yn, _, ln = oracle.softmax_rows(np.full((1, 5), -np.inf))
+    assert np.all(np.isnan(yn))
