@@ -11,14 +11,16 @@
 // N x N probabilities is the pages' account of the backward pass ("Softmax numerical
 // stability and IO-aware attention", section 7.2 and question 4).
 //
-// Three kernels, enqueued in order on one stream:
-//   1. prep: D_i = dO_i . O_i and LSE_i log2(e) per row, into the caller's workspace.
-//   2. dQ: one block per 128 query rows, 4 wavefronts of 32 rows, streaming 64-key
+// Two kernels, enqueued in order on one stream:
+//   1. dQ: one block per 128 query rows, 4 wavefronts of 32 rows, streaming 64-key
 //      tiles of K and V through LDS.  The layout is the forward's: S^T = K Q^T and
 //      dP^T = V dO^T put one query row in each lane (Q and dO fragments stay in
 //      registers), dS^T is formed in place and packed to bf16, and
-//      dQ^T += K^T dS^T reads K^T with the transposing LDS load.
-//   3. dK/dV: one block per 128 keys, 8 wavefronts (4 groups of 32 keys, two roles per
+//      dQ^T += K^T dS^T reads K^T with the transposing LDS load.  Each lane first forms
+//      D_i = dO_i . O_i for its row from the O and dO fragments (half the columns,
+//      plus the other half from its partner lane) and LSE_i log2(e), and the block
+//      writes both into the caller's workspace for the second kernel.
+//   2. dK/dV: one block per 128 keys, 8 wavefronts (4 groups of 32 keys, two roles per
 //      group), streaming 64-row tiles of Q, dO, LSE and D through LDS.  Here S = Q K^T
 //      and dP = dO V^T put one key in each lane (K or V fragments stay in registers);
 //      P and dS, packed to bf16 as they lie, are the B operands of dV^T += dO^T P and
@@ -74,8 +76,10 @@ struct BwdParams {
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
-    const float* delta;  // [B*H*N]  D_i = dO_i . O_i
-    const float* lse2;   // [B*H*N]  LSE_i * log2(e)
+    const uint16_t* o;   // the forward's output
+    const float* lse;    // the forward's LSE
+    float* delta;        // [B*H*N]  D_i = dO_i . O_i       (written by dQ, read by dK/dV)
+    float* lse2;         // [B*H*N]  LSE_i * log2(e)     (written by dQ, read by dK/dV)
     int N;
     int n_tiles;         // ceil(N / kBwdRows)
     int n_blocks;
@@ -264,35 +268,7 @@ __device__ __forceinline__ void block_coords(const BwdParams& p, bool causal, bo
 }
 
 // ---------------------------------------------------------------------------------
-// 1. D_i = dO_i . O_i and LSE_i log2(e), one row per D/8 lanes.
-// ---------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const uint16_t* o, const uint16_t* dout, const float* lse,
-                                                            float* delta, float* lse2, int64_t rows) {
-    constexpr int LPR = D / 8;  // lanes per row, 16 bytes each
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = gid / LPR;
-    const int part = (int)(gid % LPR);
-    float acc = 0.0f;
-    if (row < rows) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * part);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * part);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
-            acc = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
-        }
-    }
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && part == 0) {
-        delta[row] = acc;
-        lse2[row] = lse[row] * kLog2e;
-    }
-}
-
-// ---------------------------------------------------------------------------------
-// 2. dQ.  Lane: query row q = q0 + 32 wave + l32; S^T / dP^T rows are keys.
+// 1. dQ.  Lane: query row q = q0 + 32 wave + l32; S^T / dP^T rows are keys.
 // ---------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
@@ -326,8 +302,29 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
     bf16x8 qf[KS], dof[KS];
     load_frag<D>(qf, p.q + head, q_row, h);
     load_frag<D>(dof, p.dout + head, q_row, h);
-    const float lse2 = p.lse2[(int64_t)bh * N + q_row];
-    const float dlt = p.delta[(int64_t)bh * N + q_row];
+    // D = dO . O of the lane's row (its half of the columns here, the other half in lane
+    // l ^ 32) and LSE log2(e); the block's rows are written for the dK/dV pass.
+    float dlt = 0.0f;
+    {
+        bf16x8 of[KS];
+        load_frag<D>(of, p.o + head, q_row, h);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 a = __builtin_bit_cast(u32x4, of[ks]);
+            const u32x4 b = __builtin_bit_cast(u32x4, dof[ks]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dlt = fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), dlt);
+                dlt = fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), dlt);
+            }
+        }
+        dlt += __shfl_xor(dlt, 32, 64);
+    }
+    const float lse2 = p.lse[(int64_t)bh * N + q_row] * kLog2e;
+    if (h == 0 && my_q < N) {
+        p.delta[(int64_t)bh * N + my_q] = dlt;
+        p.lse2[(int64_t)bh * N + my_q] = lse2;
+    }
     const int key_lim = CAUSAL ? min(N - 1, my_q) : N - 1;
 
     f32x16 acc[DB];
@@ -391,7 +388,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void attn_bwd_dq_kernel(BwdParams p
 }
 
 // ---------------------------------------------------------------------------------
-// 3a. dK and dV at d = 128, the two roles pipelined.  8 wavefronts, 128 keys: key
+// 2a. dK and dV at d = 128, the two roles pipelined.  8 wavefronts, 128 keys: key
 //    group kg = wave % 4 owns keys k0 + 32 kg + l32 (one key per lane), in two roles
 //    that share a SIMD (waves w and w + 4).  The roles run one query tile apart, with
 //    one barrier per tile.  In step
@@ -643,7 +640,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void attn_bwd_dkdv_kernel(BwdParam
 }
 
 // ---------------------------------------------------------------------------------
-// 3b. dK and dV at d = 64, two phases per tile.  8 wavefronts, 128 keys: key group
+// 2b. dK and dV at d = 64, two phases per tile.  8 wavefronts, 128 keys: key group
 //    kg = wave % 4 owns keys k0 + 32 kg + l32 (one key per lane), in two roles that
 //    share a SIMD (waves w and w + 4).  Per 64-row tile of Q, dO, LSE and D:
 //      phase 1  role A (w < 4):  S = Q K^T, P = exp2(c S - LSE)  -> P to LDS (fp32)
@@ -868,6 +865,8 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
     p.k = static_cast<const uint16_t*>(k);
     p.v = static_cast<const uint16_t*>(v);
     p.dout = static_cast<const uint16_t*>(dout);
+    p.o = static_cast<const uint16_t*>(o);
+    p.lse = lse;
     p.dq = static_cast<uint16_t*>(dq);
     p.dk = static_cast<uint16_t*>(dk);
     p.dv = static_cast<uint16_t*>(dv);
@@ -881,19 +880,7 @@ hipError_t launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
     p.c = scale * kLog2e;
     p.scale = scale;
 
-    const int lpr = d / 8;
-    const int64_t prep_blocks = (rows * lpr + 255) / 256;
-    if (prep_blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (d == 64)
-        hipLaunchKernelGGL((attn_bwd_prep_kernel<64>), dim3((unsigned)prep_blocks), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(o), p.dout, lse, workspace, workspace + rows, rows);
-    else if (d == 128)
-        hipLaunchKernelGGL((attn_bwd_prep_kernel<128>), dim3((unsigned)prep_blocks), dim3(256), 0, st,
-                           static_cast<const uint16_t*>(o), p.dout, lse, workspace, workspace + rows, rows);
-    else
-        return hipErrorInvalidValue;
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (d != 64 && d != 128) return hipErrorInvalidValue;
     if (d == 64) return causal ? launch_main<64, true>(p, st) : launch_main<64, false>(p, st);
     return causal ? launch_main<128, true>(p, st) : launch_main<128, false>(p, st);
 }
