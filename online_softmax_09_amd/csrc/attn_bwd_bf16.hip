@@ -245,7 +245,7 @@ __device__ __forceinline__ void store_rows(uint16_t* out, int row, int h, const 
 // B=4 H=16 N=4096 d=128, +5% at B=2 H=32 N=8192 d=64; all of an XCD's heads at once
 // (G = 8 there) lost 1% at the first shape, and at B=1 H=32 N=16384 (4 heads per XCD)
 // pairs gained 0.7% where G = 4 lost 1%.  The price is HBM reads: four heads' streams
-// outgrow the XCD's L2 and the two kernels fetch 2.4-2.8 times their operands (0.8 TB/s
+// outgrow the XCD's L2 and the two kernels fetch 2.1-2.8 times their operands (0.8 TB/s
 // at the first shape), while both stay matrix-core bound.
 __device__ __forceinline__ void block_coords(const BwdParams& p, bool causal, bool longest_last, int& bh, int& t) {
     const int nb = p.n_blocks;
