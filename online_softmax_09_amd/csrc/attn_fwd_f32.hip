@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float* __restri
     constexpr int QPB = 256 / LPQ;    // query rows per block
     constexpr int DV = D / 64;        // float4 units of the row per lane (D / 16 dimensions)
     constexpr int BN = 32;            // keys per tile
+    static_assert(BN * (D / 4) % 256 == 0, "a tile is a whole number of float4 units per thread");
     __shared__ float4 ks[BN][D / 4];
     __shared__ float4 vs[BN][D / 4];
 
@@ -77,16 +78,32 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(const float* __restri
 
     // Causal: keys beyond the block's last query are never visible.
     const int kv_end = CAUSAL ? min(N, q0 + QPB) : N;
-    for (int j0 = 0; j0 < kv_end; j0 += BN) {
-        __syncthreads();
-        for (int idx = threadIdx.x; idx < BN * (D / 4); idx += 256) {
+    // The next tile's K and V are loaded into registers while the current one is used,
+    // so that the loop does not wait for memory once per tile.
+    constexpr int PER = BN * (D / 4) / 256;  // float4 units of a tile per thread
+    float4 kr[PER], vr[PER];
+    auto fetch = [&](int j0) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = threadIdx.x + 256 * u;
             const int r = idx / (D / 4), c = idx % (D / 4);
             const int key = j0 + r;
             const bool ok = key < N;
             const int64_t off = head + (int64_t)key * D;
-            ks[r][c] = ok ? reinterpret_cast<const float4*>(k + off)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-            vs[r][c] = ok ? reinterpret_cast<const float4*>(v + off)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            kr[u] = ok ? reinterpret_cast<const float4*>(k + off)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            vr[u] = ok ? reinterpret_cast<const float4*>(v + off)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+    };
+    fetch(0);
+    for (int j0 = 0; j0 < kv_end; j0 += BN) {
+        __syncthreads();  // the previous tile's reads of ks / vs are done
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = threadIdx.x + 256 * u;
+            ks[idx / (D / 4)][idx % (D / 4)] = kr[u];
+            vs[idx / (D / 4)][idx % (D / 4)] = vr[u];
+        }
+        if (j0 + BN < kv_end) fetch(j0 + BN);
         __syncthreads();
 
         float s[BN];
