@@ -54,8 +54,9 @@
 //   * Block ids are remapped so each of the 8 XCDs (which receive block ids round
 //     robin) walks a contiguous range of (head, query tile) pairs: the key/value
 //     stream of a head is then shared through that XCD's L2.  In causal mode an XCD
-//     takes its heads in pairs and runs each pair's query tiles longest first across
-//     the pair (at d = 64 the shortest quarter of every head's tiles comes last).
+//     takes its heads in pairs (groups of four for rows of up to 4096) and runs each
+//     group's query tiles longest first across the group (at d = 64 the shortest
+//     quarter of every head's tiles comes last).
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -358,7 +359,12 @@ __global__ __launch_bounds__(threads_of<PP>(), 2) void attn_fwd_bf16_kernel(Para
         if ((nb & 7) == 0 && per_xcd % p.n_qtiles == 0) {
             const int nq = p.n_qtiles;
             const int hx = per_xcd / nq;  // heads per XCD
-            const int G = (hx % 2 == 0) ? 2 : 1;
+            // groups of four heads for short rows (N <= 4096, with a multiple of eight heads
+            // per XCD): +6-7% at causal 4x32x2048 (d = 64 and 128), +3-6% at 8x32x1024,
+            // +0.1-0.6% at N = 4096; pairs above, where four measured +0.2-0.5% but read
+            // keys and values from memory half as often again (907 against 561 MB per
+            // call at B=2 H=32 N=8192 d=128)
+            const int G = (hx % 8 == 0 && p.N <= 4096) ? 4 : (hx % 2 == 0) ? 2 : 1;
             const int tq = D == 64 ? nq / 4 : 0;  // tiles per head held back
             const int hl = G * (nq - tq);         // tiles of one group before that
             const int x = lid / per_xcd, li = lid % per_xcd;
