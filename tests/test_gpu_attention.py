@@ -361,3 +361,20 @@ def test_causal_d64_dispatch_order(B, H, N):
     eo, el = _report("bf16", o, lse, o_ref, lse_ref, 1e-3)
     assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
     assert np.array_equal(o[:, :, 0], v[:, :, 0].float().numpy())
+
+
+@pytest.mark.parametrize("B,H,N,d", [(8, 8, 512, 64), (4, 16, 1024, 128), (2, 32, 2048, 64), (1, 64, 1000, 128)])
+def test_causal_head_groups_of_four(B, H, N, d):
+    """Causal launches of rows up to 4096 whose XCDs hold a multiple of eight heads take the
+    heads in groups of four (with the held-back shortest quarter at d = 64), a ragged N
+    included.  Every output row is compared, so a tile computed twice or never shows up."""
+    dev = need_gpu()
+    q, k, v = workloads.attention_inputs(B, H, N, d, seed=workloads.SEED_BASE + 7700 + N + H + d)
+    scale = workloads.default_scale(d)
+    say(f"case bf16 causal head groups B={B} H={H} N={N} d={d}")
+    o, lse = _gpu(osm.fa_fwd, q, k, v, scale, True, dev)
+    rows = np.broadcast_to(np.arange(N), (B, H, N))
+    o_ref, lse_ref = oracle_rows_per_head(q, k, v, scale, True, rows)
+    eo, el = _report("bf16", o, lse, o_ref, lse_ref, 1e-3)
+    assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE
+    assert np.array_equal(o[:, :, 0], v[:, :, 0].float().numpy())
