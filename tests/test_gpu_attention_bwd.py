@@ -67,7 +67,10 @@ def _compare(tag, got, ref):
     # step (N = 33; the last key block at N = 129 and 700), every remainder 0..5 (700
     # causal: 11, 9, 7, 5, 3, 1 steps; 1000 causal: 16, 14, ..., 2), a whole group and
     # nothing more (448: 7 steps)
-    (1, 1, 33, 128, True), (1, 1, 129, 128, True), (1, 1, 700, 128, True), (1, 1, 448, 128, False)])
+    (1, 1, 33, 128, True), (1, 1, 129, 128, True), (1, 1, 700, 128, True), (1, 1, 448, 128, False),
+    # causal grids with a multiple of eight heads per XCD take heads in groups of four,
+    # with four heads per XCD in pairs: every head's gradients compared
+    (1, 64, 256, 64, True), (2, 32, 300, 128, True), (1, 32, 256, 128, True)])
 def test_bwd_small_shapes(B, H, N, d, causal):
     dev = need_gpu()
     say(f"case bwd B={B} H={H} N={N} d={d} causal={causal}")
